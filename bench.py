@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention step on one MI355X.
+
+A step is one pa_step call over one synthetic batch: KV write through
+slot_mapping, split-K decode with partial reduce, and chunked prefill, over the
+flattened super-sequence. Inputs are generated on the device before timing
+and stay resident in HBM. Before each timed step a 2 GiB buffer is written so
+that no K/V is left in the 256 MB Infinity Cache or the L2s (the TinyLlama
+batch reads only ~71 MB); the flush sits outside the per-step events.
+
+Prints ONE JSON line. The headline workload is the TinyLlama-1.1B-shaped
+decode batch (64 sequences, contexts uniform in [128, 2048], 32/4 heads, head
+size 64, bf16); `value` is its decode KV-read bandwidth over the whole step.
+`secondary` holds the same measurement for the other model-shaped workloads:
+the Llama-3-8B mixed chunked-prefill + decode step (tokens/s, prefill
+TFLOP/s), the Llama-3-70B 32k decode and the shared-prefix decode.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV-read GB/s (% HBM peak), mixed-step tokens/s, prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+HEADLINE = 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def device_inputs(wl):
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    c = {
+        "q": W.q_device(wl, "cuda"),
+        "pool": W.pool_device(wl, "cuda"),
+        "slot_mapping": t(wl.slot_mapping),
+        "block_tables": t(wl.block_tables),
+        "query_start_loc": t(wl.query_start_loc),
+        "seq_lens": t(wl.seq_lens),
+        "context_lens": t(wl.context_lens),
+    }
+    c["k"], c["v"] = W.new_kv_device(wl, "cuda")
+    return c
+
+
+def measure(cfg: int, steps: int, warmup: int, flush: bool = True) -> dict:
+    import torch
+
+    import pagedattention_block_paged_amd as pa
+    import workloads as W
+
+    hbm = torch.cuda.get_device_properties(0).total_memory
+    wl = W.config_workload(cfg, hbm_bytes=hbm)
+    t0 = time.time()
+    c = device_inputs(wl)
+    torch.cuda.synchronize()
+    log(f"[bench] cfg {cfg} {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks} "
+        f"inputs ready in {time.time() - t0:.1f}s")
+    pool = c["pool"]
+    out = torch.empty_like(c["q"])
+    ws = pa.new_workspace(c["q"], pool[:, 0], c["block_tables"])
+    scratch = torch.empty(2 << 30, dtype=torch.uint8, device="cuda") if flush else None
+
+    def one_step():
+        pa.step(c["q"], c["k"], c["v"], pool[:, 0], pool[:, 1], c["slot_mapping"], c["block_tables"],
+                c["query_start_loc"], c["seq_lens"], c["context_lens"], wl.scale, out=out, workspace=ws)
+
+    for i in range(warmup):
+        if scratch is not None:
+            scratch.fill_(i & 0x7F)
+        one_step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_wall = time.perf_counter()
+    with pa.profile() as prof:
+        for i in range(steps):
+            if scratch is not None:
+                scratch.fill_(i & 0x7F)
+            starts[i].record()
+            one_step()
+            ends[i].record()
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    ms = sum(per) / len(per)
+    finite = bool(torch.isfinite(out.float()).all())
+    kern = {k: {"avg_ms": v[0] / v[1], "launches": v[1]} for k, v in prof.kernels.items()}
+    dec_bytes = wl.decode_bytes()
+    dec_kernel_bytes = dec_bytes - W.DTYPE_BYTES[wl.dtype] * int(wl.decode_mask().sum()) * wl.num_q_heads * \
+        wl.head_size  # the decode kernel reads KV, tables and q; outputs are written by it or the reduce
+    flops = wl.prefill_flops()
+    r = {
+        "workload": wl.name,
+        "num_seqs": wl.num_seqs,
+        "num_tokens": wl.num_tokens,
+        "num_q_heads": wl.num_q_heads,
+        "num_kv_heads": wl.num_kv_heads,
+        "head_size": wl.head_size,
+        "dtype": wl.dtype,
+        "pool_blocks": wl.num_blocks,
+        "partition_tokens": pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_blocks),
+        "ms_per_step": ms,
+        "ms_per_step_median": per[len(per) // 2],
+        "ms_per_step_min": per[0],
+        "wall_s_timed_region": wall,
+        "tokens_per_s": wl.num_tokens / (ms * 1e-3),
+        "decode_bytes": dec_bytes,
+        "decode_gbs_step": dec_bytes / (ms * 1e-3) / 1e9,
+        "prefill_flops": flops,
+        "kernels": kern,
+        "output_finite": finite,
+    }
+    if "decode" in kern:
+        d = kern["decode"]["avg_ms"]
+        r["decode_kernel_bytes"] = dec_kernel_bytes
+        r["decode_kernel_gbs"] = dec_kernel_bytes / (d * 1e-3) / 1e9
+        r["decode_kernel_hbm_frac"] = r["decode_kernel_gbs"] / HBM_PEAK_GBS
+    if flops and "prefill" in kern:
+        p = kern["prefill"]["avg_ms"]
+        r["prefill_tflops"] = flops / (p * 1e-3) / 1e12
+        r["prefill_mfma_frac"] = r["prefill_tflops"] / BF16_PEAK_TFLOPS
+    del c, pool, out, ws, scratch
+    torch.cuda.empty_cache()
+    return r
+
+
+def cpu_baseline(cfg: int, budget_s: float) -> dict:
+    """The oracle, as is, on the host cores: write + attention over the whole batch, repeated."""
+    import oracle
+    import workloads as W
+
+    wl = W.config_workload(cfg)
+    pool0 = W.pool_host(wl)
+    k, v = W.new_kv_host(wl)
+    q = W.q_host(wl)
+    passes, threads, t0 = 0, 0, time.perf_counter()
+    while True:
+        pool = pool0.copy()
+        a = time.perf_counter()
+        oracle.reshape_and_cache(k, v, pool, wl.slot_mapping, wl.dtype)
+        _, threads = oracle.attention(q, pool, wl.block_tables, wl.query_start_loc, wl.seq_lens, wl.context_lens,
+                                      wl.scale, wl.dtype, return_threads=True)
+        passes += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s:
+            break
+    secs = elapsed  # includes the pool copy per pass (a few ms)
+    return {
+        "value": wl.decode_bytes() * passes / secs / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"whole {wl.name} batch ({wl.num_seqs} sequences), KV write + attention, {passes} passes "
+                  f"in {secs:.1f} s, fp64, {threads} OpenMP threads",
+        "tokens_per_s": wl.num_tokens * passes / secs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
+    ap.add_argument("--secondary", default="3,4,5", help="other workloads to measure, or 'none'")
+    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import pagedattention_block_paged_amd  # noqa: F401  (fails loudly if libpa.so is missing)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    head = measure(args.config, args.steps, args.warmup, flush=not args.no_flush)
+    log(f"[bench] headline: {json.dumps(head)}")
+    secondary = {}
+    if args.secondary != "none":
+        for cfg in [int(x) for x in args.secondary.split(",") if x]:
+            if cfg == args.config:
+                continue
+            r = measure(cfg, args.secondary_steps, 1, flush=not args.no_flush)
+            log(f"[bench] cfg {cfg}: {json.dumps(r)}")
+            secondary[r["workload"]] = r
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 x 1 GiB device-to-device copies")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.config, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {json.dumps(cpu)}")
+
+    dec = head.get("decode_kernel_gbs")
+    line = {
+        "metric": METRIC,
+        "value": head["decode_gbs_step"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {
+            "workload": head["workload"],
+            "num_seqs": head["num_seqs"],
+            "num_tokens": head["num_tokens"],
+            "num_q_heads": head["num_q_heads"],
+            "num_kv_heads": head["num_kv_heads"],
+            "head_size": head["head_size"],
+            "block_size": 16,
+            "pool_blocks": head["pool_blocks"],
+            "parallelism": "single GPU",
+        },
+        "hbm_frac_step": head["decode_gbs_step"] / HBM_PEAK_GBS,
+        "roofline": {
+            "kernel": "decode",
+            "bound": "hbm",
+            "achieved": dec,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": (dec / HBM_PEAK_GBS) if dec else None,
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "kernels": head["kernels"],
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

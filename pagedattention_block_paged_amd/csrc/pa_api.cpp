@@ -1,0 +1,387 @@
+// C-ABI entry points of libpa.so: host-side validation of the tensor
+// descriptors, workspace layout, and dispatch to the HIP kernel launchers.
+// Nothing here touches device memory or synchronises the device, so every
+// validation path runs (and is tested) on a machine without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status ok() {
+  g_last_error.clear();
+  return PA_OK;
+}
+
+int64_t elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_I32: return 4;
+    case PA_I64: return 8;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return "f32";
+    case PA_BF16: return "bf16";
+    case PA_I32: return "i32";
+    case PA_I64: return "i64";
+    default: return "?";
+  }
+}
+
+int64_t numel(const pa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Descriptor sanity: present, rank, dtype, non-negative extents, data present
+// unless empty.
+pa_status check_desc(const pa_tensor* t, const char* name, int ndim) {
+  if (!t) return fail(PA_ERR_NULL, "%s: descriptor is NULL", name);
+  if (t->ndim != ndim) return fail(PA_ERR_SHAPE, "%s: expected %d dims, got %d", name, ndim, t->ndim);
+  if (elem_bytes(t->dtype) == 0) return fail(PA_ERR_DTYPE, "%s: unknown dtype %d", name, t->dtype);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return fail(PA_ERR_SHAPE, "%s: negative extent in dim %d", name, i);
+  if (!t->data && numel(t) > 0) return fail(PA_ERR_NULL, "%s: data pointer is NULL", name);
+  return PA_OK;
+}
+
+pa_status check_dtype(const pa_tensor* t, const char* name, int32_t want) {
+  if (t->dtype != want)
+    return fail(PA_ERR_DTYPE, "%s: dtype %s, expected %s", name, dtype_name(t->dtype), dtype_name(want));
+  return PA_OK;
+}
+
+// A float tensor whose last dim is contiguous and whose rows are 16-byte
+// aligned (the kernels move rows in 16-byte vectors).
+pa_status check_rows(const pa_tensor* t, const char* name) {
+  if (t->stride[t->ndim - 1] != 1 && t->shape[t->ndim - 1] > 1)
+    return fail(PA_ERR_STRIDE, "%s: last dim must be contiguous (stride %lld)", name,
+                (long long)t->stride[t->ndim - 1]);
+  const int64_t es = elem_bytes(t->dtype);
+  if (reinterpret_cast<uintptr_t>(t->data) % 16)
+    return fail(PA_ERR_STRIDE, "%s: data pointer not 16-byte aligned", name);
+  for (int i = 0; i + 1 < t->ndim; ++i)
+    if ((t->stride[i] * es) % 16 || t->stride[i] < 0)
+      return fail(PA_ERR_STRIDE, "%s: stride of dim %d (%lld elements) is not a multiple of 16 bytes", name, i,
+                  (long long)t->stride[i]);
+  return PA_OK;
+}
+
+pa_status check_contig1(const pa_tensor* t, const char* name) {
+  if (t->shape[0] > 1 && t->stride[0] != 1) return fail(PA_ERR_STRIDE, "%s: must be contiguous", name);
+  return PA_OK;
+}
+
+#define PA_TRY(expr)                  \
+  do {                                \
+    pa_status _st = (expr);           \
+    if (_st != PA_OK) return _st;     \
+  } while (0)
+
+struct CacheShape {
+  int64_t NB, Hkv, D;
+  int32_t dtype;
+};
+
+pa_status check_caches(const pa_tensor* kc, const pa_tensor* vc, CacheShape* cs) {
+  PA_TRY(check_desc(kc, "key_cache", 4));
+  PA_TRY(check_desc(vc, "value_cache", 4));
+  if (kc->dtype != PA_F32 && kc->dtype != PA_BF16)
+    return fail(PA_ERR_DTYPE, "key_cache: dtype %s, expected f32 or bf16", dtype_name(kc->dtype));
+  PA_TRY(check_dtype(vc, "value_cache", kc->dtype));
+  for (int i = 0; i < 4; ++i)
+    if (kc->shape[i] != vc->shape[i]) return fail(PA_ERR_SHAPE, "key_cache and value_cache shapes differ (dim %d)", i);
+  if (kc->shape[1] != pa::kBlockTokens)
+    return fail(PA_ERR_UNSUPPORTED, "block size %lld not supported (only 16)", (long long)kc->shape[1]);
+  if (kc->shape[0] < 1) return fail(PA_ERR_SHAPE, "key_cache: pool has no blocks");
+  PA_TRY(check_rows(kc, "key_cache"));
+  PA_TRY(check_rows(vc, "value_cache"));
+  cs->NB = kc->shape[0];
+  cs->Hkv = kc->shape[2];
+  cs->D = kc->shape[3];
+  cs->dtype = kc->dtype;
+  if (cs->Hkv < 1 || cs->D < 1) return fail(PA_ERR_SHAPE, "key_cache: empty head dims");
+  return PA_OK;
+}
+
+pa_status validate_write(const pa_tensor* k, const pa_tensor* v, const pa_tensor* kc, const pa_tensor* vc,
+                         const pa_tensor* slots, pa::WriteArgs* a) {
+  CacheShape cs;
+  PA_TRY(check_caches(kc, vc, &cs));
+  PA_TRY(check_desc(k, "k", 3));
+  PA_TRY(check_desc(v, "v", 3));
+  PA_TRY(check_desc(slots, "slot_mapping", 1));
+  PA_TRY(check_dtype(k, "k", cs.dtype));
+  PA_TRY(check_dtype(v, "v", cs.dtype));
+  PA_TRY(check_dtype(slots, "slot_mapping", PA_I64));
+  const int64_t T = k->shape[0];
+  for (int i = 0; i < 3; ++i)
+    if (k->shape[i] != v->shape[i]) return fail(PA_ERR_SHAPE, "k and v shapes differ (dim %d)", i);
+  if (k->shape[1] != cs.Hkv || k->shape[2] != cs.D)
+    return fail(PA_ERR_SHAPE, "k is [%lld, %lld, %lld], cache heads/dims are [%lld, %lld]", (long long)T,
+                (long long)k->shape[1], (long long)k->shape[2], (long long)cs.Hkv, (long long)cs.D);
+  if (slots->shape[0] != T)
+    return fail(PA_ERR_SHAPE, "slot_mapping has %lld entries for %lld tokens", (long long)slots->shape[0],
+                (long long)T);
+  const int64_t es = elem_bytes(cs.dtype);
+  if ((cs.D * es) % 16) return fail(PA_ERR_UNSUPPORTED, "head_size %lld: rows must be a multiple of 16 bytes",
+                                    (long long)cs.D);
+  PA_TRY(check_contig1(slots, "slot_mapping"));
+  if (T > 0) {
+    PA_TRY(check_rows(k, "k"));
+    PA_TRY(check_rows(v, "v"));
+  }
+  a->k = static_cast<const char*>(k->data);
+  a->v = static_cast<const char*>(v->data);
+  a->kc = static_cast<char*>(kc->data);
+  a->vc = static_cast<char*>(vc->data);
+  a->slots = static_cast<const int64_t*>(slots->data);
+  a->T = T;
+  a->Hkv = cs.Hkv;
+  a->D = cs.D;
+  a->NB = cs.NB;
+  a->k_st = k->stride[0] * es;
+  a->k_sh = k->stride[1] * es;
+  a->v_st = v->stride[0] * es;
+  a->v_sh = v->stride[1] * es;
+  a->kc_sb = kc->stride[0] * es;
+  a->kc_sr = kc->stride[1] * es;
+  a->kc_sh = kc->stride[2] * es;
+  a->vc_sb = vc->stride[0] * es;
+  a->vc_sr = vc->stride[1] * es;
+  a->vc_sh = vc->stride[2] * es;
+  a->es = static_cast<int>(es);
+  return PA_OK;
+}
+
+pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc,
+                             const pa_tensor* bt, const pa_tensor* qsl, const pa_tensor* sl, const pa_tensor* cl,
+                             float scale, void* ws, size_t ws_bytes, pa::AttnArgs* a) {
+  CacheShape cs;
+  PA_TRY(check_caches(kc, vc, &cs));
+  PA_TRY(check_desc(out, "out", 3));
+  PA_TRY(check_desc(q, "q", 3));
+  PA_TRY(check_desc(bt, "block_tables", 2));
+  PA_TRY(check_desc(qsl, "query_start_loc", 1));
+  PA_TRY(check_desc(sl, "seq_lens", 1));
+  PA_TRY(check_desc(cl, "context_lens", 1));
+  PA_TRY(check_dtype(q, "q", cs.dtype));
+  PA_TRY(check_dtype(out, "out", cs.dtype));
+  PA_TRY(check_dtype(bt, "block_tables", PA_I32));
+  PA_TRY(check_dtype(qsl, "query_start_loc", PA_I32));
+  PA_TRY(check_dtype(sl, "seq_lens", PA_I32));
+  PA_TRY(check_dtype(cl, "context_lens", PA_I32));
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(PA_ERR_SHAPE, "out and q shapes differ (dim %d)", i);
+  if (D != cs.D) return fail(PA_ERR_SHAPE, "q head_size %lld != cache head_size %lld", (long long)D, (long long)cs.D);
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_size %lld not supported (64 or 128)", (long long)D);
+  if (Hq < 1 || Hq % cs.Hkv)
+    return fail(PA_ERR_SHAPE, "num_q_heads %lld is not a multiple of num_kv_heads %lld", (long long)Hq,
+                (long long)cs.Hkv);
+  if (Hq / cs.Hkv > 16)
+    return fail(PA_ERR_UNSUPPORTED, "query heads per KV head %lld > 16", (long long)(Hq / cs.Hkv));
+  const int64_t S = bt->shape[0], MB = bt->shape[1];
+  if (MB < 1) return fail(PA_ERR_SHAPE, "block_tables has no columns");
+  if (qsl->shape[0] != S + 1)
+    return fail(PA_ERR_SHAPE, "query_start_loc has %lld entries for %lld sequences", (long long)qsl->shape[0],
+                (long long)S);
+  if (sl->shape[0] != S || cl->shape[0] != S) return fail(PA_ERR_SHAPE, "seq_lens/context_lens must have S entries");
+  if (bt->stride[1] != 1 && MB > 1) return fail(PA_ERR_STRIDE, "block_tables rows must be contiguous");
+  if (bt->stride[0] < MB && S > 1) return fail(PA_ERR_STRIDE, "block_tables rows overlap");
+  PA_TRY(check_contig1(qsl, "query_start_loc"));
+  PA_TRY(check_contig1(sl, "seq_lens"));
+  PA_TRY(check_contig1(cl, "context_lens"));
+  if (T > 0) {
+    PA_TRY(check_rows(q, "q"));
+    PA_TRY(check_rows(out, "out"));
+  }
+  if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  const pa::WorkspaceLayout wl = pa::workspace_layout(S, T, Hq, cs.Hkv, D, MB);
+  if (ws_bytes < wl.total)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, wl.total);
+  if (wl.total > 0 && !ws) return fail(PA_ERR_WORKSPACE, "workspace pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
+
+  const int64_t es = elem_bytes(cs.dtype);
+  a->out = static_cast<char*>(out->data);
+  a->q = static_cast<const char*>(q->data);
+  a->kc = static_cast<const char*>(kc->data);
+  a->vc = static_cast<const char*>(vc->data);
+  a->block_tables = static_cast<const int32_t*>(bt->data);
+  a->qsl = static_cast<const int32_t*>(qsl->data);
+  a->seq_lens = static_cast<const int32_t*>(sl->data);
+  a->ctx_lens = static_cast<const int32_t*>(cl->data);
+  a->T = T;
+  a->S = S;
+  a->MB = MB;
+  a->NB = cs.NB;
+  a->Hq = Hq;
+  a->Hkv = cs.Hkv;
+  a->D = D;
+  a->out_st = out->stride[0] * es;
+  a->out_sh = out->stride[1] * es;
+  a->q_st = q->stride[0] * es;
+  a->q_sh = q->stride[1] * es;
+  a->kc_sb = kc->stride[0] * es;
+  a->kc_sr = kc->stride[1] * es;
+  a->kc_sh = kc->stride[2] * es;
+  a->vc_sb = vc->stride[0] * es;
+  a->vc_sr = vc->stride[1] * es;
+  a->vc_sh = vc->stride[2] * es;
+  a->bt_row = S > 1 ? bt->stride[0] : MB;
+  a->scale = scale;
+  a->elem = cs.dtype == PA_F32 ? pa::Elem::F32 : pa::Elem::BF16;
+  a->part_tokens = pa::partition_tokens(S, cs.Hkv, MB);
+  a->max_parts = (MB * pa::kBlockTokens + a->part_tokens - 1) / a->part_tokens;
+  char* base = static_cast<char*>(ws);
+  a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
+  a->ws_ml = reinterpret_cast<float2*>(base + wl.ml_off);
+  a->ws_o = reinterpret_cast<float*>(base + wl.o_off);
+  return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream) {
+  if (a.S == 0 || a.T == 0) return PA_OK;
+  PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
+  PA_TRY(hip_status(pa::launch_prefill(a, stream), "prefill launch"));
+  return PA_OK;
+}
+
+}  // namespace
+
+namespace pa {
+
+int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
+  static const int64_t forced = [] {
+    const char* e = std::getenv("PA_PARTITION_TOKENS");
+    if (!e) return int64_t(0);
+    long long v = std::atoll(e);
+    return (v >= kBlockTokens && v % kBlockTokens == 0) ? int64_t(v) : int64_t(0);
+  }();
+  if (forced) return forced;
+  // Largest partition that still gives about 16 waves per CU on the
+  // longest possible sequences (256 CUs): long contexts get long partitions
+  // (fewer partial results), short batches get more parallel work.
+  const int64_t max_len = MB * kBlockTokens;
+  for (int64_t pt : {1024, 512, 256, 128}) {
+    const int64_t parts = (max_len + pt - 1) / pt;
+    if (S * Hkv * parts >= 4096) return pt;
+  }
+  return 128;
+}
+
+WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB) {
+  (void)T;
+  auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
+  WorkspaceLayout w{};
+  const int64_t pt = partition_tokens(S, Hkv, MB);
+  const int64_t parts = (MB * kBlockTokens + pt - 1) / pt;
+  w.tile_start_off = 0;
+  w.ml_off = align(size_t(S + 1) * sizeof(int32_t));
+  w.o_off = w.ml_off + align(size_t(S) * Hq * parts * sizeof(float2));
+  w.total = w.o_off + align(size_t(S) * Hq * parts * D * sizeof(float));
+  return w;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
+                               const pa_tensor* value_cache, const pa_tensor* slot_mapping, pa_stream stream) {
+  pa::WriteArgs a{};
+  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, &a));
+  if (a.T == 0) return ok();
+  PA_TRY(hip_status(pa::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv write launch"));
+  return ok();
+}
+
+pa_status pa_attention(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
+                       const pa_tensor* value_cache, const pa_tensor* block_tables,
+                       const pa_tensor* query_start_loc, const pa_tensor* seq_lens, const pa_tensor* context_lens,
+                       float scale, void* workspace, size_t workspace_bytes, pa_stream stream) {
+  pa::AttnArgs a{};
+  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
+                            scale, workspace, workspace_bytes, &a));
+  PA_TRY(run_attention(a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                  const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                  const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                  const pa_tensor* context_lens, float scale, void* workspace, size_t workspace_bytes,
+                  pa_stream stream) {
+  pa::WriteArgs w{};
+  pa::AttnArgs a{};
+  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, &w));
+  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
+                            scale, workspace, workspace_bytes, &a));
+  if (w.T != a.T)
+    return fail(PA_ERR_SHAPE, "k has %lld tokens, q has %lld", (long long)w.T, (long long)a.T);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
+  PA_TRY(run_attention(a, s));
+  return ok();
+}
+
+size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads, int64_t num_kv_heads,
+                                   int64_t head_size, int64_t max_blocks_per_seq) {
+  if (num_seqs < 0 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 || head_size < 1 ||
+      max_blocks_per_seq < 1)
+    return 0;
+  return pa::workspace_layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq).total;
+}
+
+int64_t pa_partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq) {
+  return pa::partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq);
+}
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "null pointer";
+    case PA_ERR_DTYPE: return "wrong or inconsistent element type";
+    case PA_ERR_SHAPE: return "inconsistent shapes";
+    case PA_ERR_STRIDE: return "unsupported layout or alignment";
+    case PA_ERR_UNSUPPORTED: return "unsupported size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_version(void) { return 100; }
+
+}  // extern "C"

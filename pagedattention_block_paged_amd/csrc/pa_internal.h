@@ -1,0 +1,84 @@
+// Internal interface between the C-ABI layer (pa_api.cpp) and the HIP kernel
+// launchers (kv_write.hip, decode.hip, prefill.hip). Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pa {
+
+constexpr int kBlockTokens = 16;  // token slots per KV block
+constexpr int kWaves = 4;         // waves per workgroup in every kernel
+constexpr int kThreads = 64 * kWaves;
+
+enum class Elem : int { F32 = 0, BF16 = 1 };
+
+// KV write: all strides in bytes.
+struct WriteArgs {
+  const char* k;
+  const char* v;
+  char* kc;
+  char* vc;
+  const int64_t* slots;
+  int64_t T, Hkv, D, NB;
+  int64_t k_st, k_sh, v_st, v_sh;        // k/v: token and head strides
+  int64_t kc_sb, kc_sr, kc_sh;           // key cache: block, row, head strides
+  int64_t vc_sb, vc_sr, vc_sh;           // value cache
+  int es;                                // element bytes
+};
+
+// Attention: all tensor strides in bytes except the int32 tables (elements).
+struct AttnArgs {
+  char* out;
+  const char* q;
+  const char* kc;
+  const char* vc;
+  const int32_t* block_tables;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* ctx_lens;
+  int64_t T, S, MB, NB, Hq, Hkv, D;
+  int64_t out_st, out_sh, q_st, q_sh;
+  int64_t kc_sb, kc_sr, kc_sh, vc_sb, vc_sr, vc_sh;
+  int64_t bt_row;  // block-table row stride (elements)
+  float scale;
+  Elem elem;
+  // split-K decode
+  int64_t part_tokens;  // tokens per partition (multiple of 16)
+  int64_t max_parts;    // partitions per sequence at most: ceil(MB * 16 / part_tokens)
+  float* ws_o;          // [S][Hq][max_parts][D] unnormalised partial outputs
+  float2* ws_ml;        // [S][Hq][max_parts] (running max in log2 units, sum of weights)
+  // prefill work list
+  int32_t* tile_start;  // [S + 1] exclusive prefix sum of prefill q-tiles per sequence
+};
+
+struct WorkspaceLayout {
+  size_t tile_start_off, ml_off, o_off, total;
+};
+
+int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB);
+WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB);
+
+// Optional per-kernel HIP-event timing (include/pa_profile.h).
+enum KernelId { kKvWrite = 0, kDecode = 1, kReduce = 2, kPlan = 3, kPrefill = 4 };
+bool profiling();
+void profile_mark(int id, bool end, hipStream_t stream);
+struct ProfileScope {
+  int id;
+  hipStream_t stream;
+  bool on;
+  ProfileScope(int id_, hipStream_t s) : id(id_), stream(s), on(profiling()) {
+    if (on) profile_mark(id, false, stream);
+  }
+  ~ProfileScope() {
+    if (on) profile_mark(id, true, stream);
+  }
+};
+
+hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pa

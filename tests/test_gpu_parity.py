@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bounds: KV write bit-exact; fp32 max abs <= 1e-5; bf16 max abs <= 2e-2, mean
+abs <= 1e-2 and per-row max|err| <= 3e-2 * rms (tests/parity.py). The five
+model-shaped workloads run at full size in the launch configuration the
+benchmark times; the oracle checks every row for the small ones and a sample
+of whole sequences (always the longest and shortest) for the large ones.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import device_case, raw_bytes, rows_of, run_step, sample_seqs, to_f64
+from parity import assert_within
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import pagedattention_block_paged_amd as lib
+
+    return lib
+
+
+def hbm_bytes():
+    return torch.cuda.get_device_properties(0).total_memory
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_write(wl, c, pool_after, k, v):
+    """Written rows equal k/v bit for bit."""
+    sm = torch.from_numpy(wl.slot_mapping).cuda()
+    keep = sm >= 0
+    blk, row = (sm // 16)[keep], (sm % 16)[keep]
+    assert torch.equal(pool_after[blk, 0, row].view(torch.int16 if wl.dtype == "bf16" else torch.int32),
+                       k[keep].view(torch.int16 if wl.dtype == "bf16" else torch.int32))
+    assert torch.equal(pool_after[blk, 1, row].view(torch.int16 if wl.dtype == "bf16" else torch.int32),
+                       v[keep].view(torch.int16 if wl.dtype == "bf16" else torch.int32))
+
+
+def row_checksums(pool, dtype, chunk=16384):
+    """Per-(block, K|V, row) checksums of the raw bits, int64 [NB, 2, 16, 2]."""
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    outs = []
+    for a in range(0, pool.shape[0], chunk):
+        x = pool[a:a + chunk].view(iv).to(torch.int64)
+        outs.append(torch.stack([x.sum(dim=(-1, -2)), (x * x).sum(dim=(-1, -2))], dim=-1))
+    return torch.cat(outs)
+
+
+def oracle_rows(wl, seqs):
+    sub = W.sub_workload(wl, seqs)
+    out, _ = oracle.run_workload(sub)
+    return out
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_config_parity(pa, cfg):
+    wl = W.config_workload(cfg, hbm_bytes=hbm_bytes())
+    say(f"[cfg {cfg}] {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
+    c = device_case(wl)
+    small = wl.num_blocks * wl.block_bytes <= (1 << 30)
+    before = raw_bytes(c["pool"]) if small else None
+    sums_before = None if small else row_checksums(c["pool"], wl.dtype)
+    out = run_step(pa, wl, c)
+    torch.cuda.synchronize()
+    check_write(wl, c, c["pool"], c["k"], c["v"])
+    # every row the write did not target is unchanged
+    touched = np.zeros((wl.num_blocks, 16), bool)
+    sm = wl.slot_mapping[wl.slot_mapping >= 0]
+    touched[sm // 16, sm % 16] = True
+    if small:
+        after = raw_bytes(c["pool"]).reshape(wl.num_blocks, 2, 16, -1).transpose(0, 2, 1, 3)
+        ref = before.reshape(wl.num_blocks, 2, 16, -1).transpose(0, 2, 1, 3)
+        assert np.array_equal(after[~touched], ref[~touched])
+    else:
+        sums_after = row_checksums(c["pool"], wl.dtype)
+        mask = torch.from_numpy(~touched).cuda()
+        assert torch.equal(sums_after.permute(0, 2, 1, 3)[mask], sums_before.permute(0, 2, 1, 3)[mask])
+    # attention
+    seqs = list(range(wl.num_seqs)) if wl.num_seqs <= 64 else sample_seqs(wl, {3: 10, 4: 3}.get(cfg, 6))
+    say(f"[cfg {cfg}] oracle on {len(seqs)} sequences")
+    ref = oracle_rows(wl, seqs)
+    got = to_f64(out[torch.from_numpy(rows_of(wl, seqs)).cuda()])
+    e = assert_within(got, ref, wl.dtype, f"cfg {cfg}")
+    say(f"[cfg {cfg}] {e}")
+
+
+def test_single_key_output_is_its_value(pa):
+    wl = W.config_workload(1)
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    s = list(wl.seq_lens).index(1)
+    t = int(wl.query_start_loc[s])
+    G = wl.num_q_heads // wl.num_kv_heads
+    want = c["v"][t].repeat_interleave(G, dim=0)
+    assert torch.equal(out[t], want)
+
+
+def mixes():
+    cases = []
+    rs = np.random.default_rng(1234)
+    shapes = [(4, 2, 64, "f32"), (8, 8, 64, "bf16"), (16, 1, 128, "bf16"), (12, 4, 128, "f32"),
+              (32, 8, 128, "bf16"), (6, 2, 64, "bf16"), (4, 4, 128, "f32"), (64, 8, 128, "bf16")]
+    for i, (Hq, Hkv, D, dt) in enumerate(shapes):
+        S = int(rs.integers(1, 7))
+        ctx, ql = [], []
+        for _ in range(S):
+            if rs.random() < 0.5:
+                ctx.append(int(rs.integers(0, 700)))
+                ql.append(1)
+            else:
+                ctx.append(int(rs.integers(0, 300)))
+                ql.append(int(rs.integers(2, 150)))
+        cases.append(W.build_workload(f"mix{i}", dt, Hq, Hkv, D, ctx, ql, seed=500 + i))
+    return cases
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_random_mixes(pa, idx):
+    wl = mixes()[idx]
+    say(f"[mix {idx}] {wl.dtype} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_size} "
+        f"ctx={wl.context_lens.tolist()} q={wl.query_lens.tolist()}")
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    ref, pool_ref = oracle.run_workload(wl)
+    assert np.array_equal(raw_bytes(c["pool"]), pool_ref.view(np.uint8).reshape(-1))
+    e = assert_within(to_f64(out), ref, wl.dtype, f"mix {idx}")
+    say(f"[mix {idx}] {e}")
+
+
+def test_chunked_prefill_matches_whole_prefill(pa):
+    """18 tokens as chunks of 8 + 8 + 2 through one pool equal one 18-token prefill."""
+    whole = W.build_workload("whole", "bf16", 8, 2, 128, [0], [18], seed=77, num_blocks=8)
+    c = device_case(whole)
+    out_whole = run_step(pa, whole, c).clone()
+    c2 = device_case(whole)  # fresh pool, nothing cached
+    done, rows = 0, []
+    for n in (8, 8, 2):
+        qsl = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+        sl = torch.tensor([done + n], dtype=torch.int32, device="cuda")
+        cl = torch.tensor([done], dtype=torch.int32, device="cuda")
+        pool = c2["pool"]
+        rows.append(pa.step(c2["q"][done:done + n].contiguous(), c2["k"][done:done + n].contiguous(),
+                            c2["v"][done:done + n].contiguous(), pool[:, 0], pool[:, 1],
+                            c2["slot_mapping"][done:done + n].contiguous(), c2["block_tables"], qsl, sl, cl,
+                            whole.scale))
+        done += n
+    torch.cuda.synchronize()
+    got = torch.cat(rows)
+    ref, _ = oracle.run_workload(whole)
+    assert_within(to_f64(got), ref, "bf16", "chunked")
+    assert_within(to_f64(out_whole), ref, "bf16", "whole")
+
+
+def test_physical_permutation_is_bit_exact(pa):
+    wl = W.config_workload(2)
+    c = device_case(wl)
+    out = run_step(pa, wl, c).clone()
+    pi = np.random.default_rng(3).permutation(wl.num_blocks)
+    wl_p = W.with_block_tables(wl, pi[wl.block_tables], wl.num_blocks, int(pi[wl.canary_block]))
+    cp = device_case(wl_p)
+    pool = W.pool_device(wl, "cuda")
+    cp["pool"][torch.from_numpy(pi).cuda()] = pool
+    out_p = run_step(pa, wl_p, cp)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_p.view(torch.int16))
+
+
+def test_shared_prefix_blocks_equal_private_copies_bit_exact(pa):
+    wl = W.config_workload(5)
+    c = device_case(wl)
+    out = run_step(pa, wl, c).clone()
+    n_sh = 128
+    NB2 = wl.num_blocks + wl.num_seqs * n_sh
+    tables = np.concatenate([wl.block_tables, np.zeros((wl.num_seqs, 0), np.int32)], axis=1).astype(np.int64)
+    shared_ids = wl.block_tables[0, :n_sh].astype(np.int64)
+    for s in range(wl.num_seqs):
+        tables[s, :n_sh] = wl.num_blocks + s * n_sh + np.arange(n_sh)
+    wl_p = W.with_block_tables(wl, tables, NB2, wl.canary_block)
+    cp = device_case(wl_p)
+    base = W.pool_device(wl, "cuda")
+    cp["pool"][: wl.num_blocks] = base
+    src = torch.from_numpy(shared_ids).cuda()
+    for s in range(wl.num_seqs):
+        cp["pool"][wl.num_blocks + s * n_sh: wl.num_blocks + (s + 1) * n_sh] = base[src]
+    out_p = run_step(pa, wl_p, cp)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_p.view(torch.int16))
+
+
+def test_repeated_calls_are_deterministic(pa):
+    wl = W.sub_workload(W.config_workload(3), [0, 1, 2, 4096, 4097])
+    c = device_case(wl)
+    ws = pa.new_workspace(c["q"], c["pool"][:, 0], c["block_tables"])
+    a = run_step(pa, wl, c, workspace=ws).clone()
+    b = run_step(pa, wl, c, workspace=ws).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("delta", [-1, 0, 1, 17])
+def test_split_partition_boundaries(pa, delta):
+    """Decode lengths around multiples of the partition size."""
+    pt = pa.partition_tokens(4, 2, 256)
+    L = [pt + delta, 2 * pt + delta, 3 * pt + delta, 1]
+    L = [max(1, x) for x in L]
+    wl = W.build_workload("split", "bf16", 16, 2, 128, np.array(L) - 1, [1, 1, 1, 1], seed=40 + delta,
+                          max_blocks=256)
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    ref, _ = oracle.run_workload(wl)
+    assert_within(to_f64(out), ref, "bf16", f"split {pt}+{delta}")
+
+
+def test_empty_batch_is_a_no_op(pa):
+    q = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((0, 2, 64), dtype=torch.bfloat16, device="cuda")
+    pool = pa.new_kv_pool(4, 2, 64)
+    z = lambda n: torch.zeros(n, dtype=torch.int32, device="cuda")
+    out = pa.step(q, kv, kv, pool[:, 0], pool[:, 1], torch.empty(0, dtype=torch.int64, device="cuda"),
+                  torch.zeros((0, 1), dtype=torch.int32, device="cuda"), z(1), z(0), z(0), 0.125)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 8, 64)
+
+
+def test_sequence_without_queries_and_padding_slot(pa):
+    """A sequence with no query rows is skipped; a padding token (slot -1) writes nothing."""
+    wl = W.build_workload("gap", "bf16", 8, 2, 64, [40, 30, 20], [1, 1, 3], seed=9)
+    c = device_case(wl)
+    # give sequence 1 zero queries: drop its token from the batch, keep its row count
+    keep = [0, 2, 3, 4]
+    q = c["q"][keep].contiguous()
+    k = c["k"][keep].contiguous()
+    v = c["v"][keep].contiguous()
+    sm = c["slot_mapping"][keep].clone()
+    sm[0] = -1  # sequence 0's new token is padding: not written
+    qsl = torch.tensor([0, 1, 1, 4], dtype=torch.int32, device="cuda")
+    pool = c["pool"]
+    before = pool.clone()
+    out = pa.step(q, k, v, pool[:, 0], pool[:, 1], sm, c["block_tables"], qsl, c["seq_lens"], c["context_lens"],
+                  wl.scale)
+    torch.cuda.synchronize()
+    s0 = int(wl.slot_mapping[0])
+    assert torch.equal(pool[s0 // 16, :, s0 % 16].view(torch.int16), before[s0 // 16, :, s0 % 16].view(torch.int16))
+    ref, _ = oracle.run_workload(W.sub_workload(wl, [2]))
+    assert_within(to_f64(out[1:4]), ref, "bf16", "after gap")
