@@ -204,9 +204,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       pr[r] = fast_exp2(sc[r] - m_run);
       l_run += pr[r];
     }
-    // O[head][d = VE * n + e] += sum over the 4 lane groups of P[head][token] V[token][d]
+    // O[head][d = VE * n + e] += sum over the 4 lane groups of P[head][token] V[token][d].
+    // Rows past the sequence end carry weight 0 but arbitrary bits (0 * NaN is
+    // NaN), so they are zeroed before the product.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      if (tok0 + j >= end) {
+#pragma unroll
+        for (int w = 0; w < Sh::VW; ++w) cur.v[j][w] = 0u;
+      }
       float vf[VE];
       widen<BF16, VE, Sh::VW>(cur.v[j], vf);
 #pragma unroll

@@ -33,10 +33,11 @@ def to_f64(x: torch.Tensor) -> np.ndarray:
 
 
 def raw_bytes(x: torch.Tensor) -> np.ndarray:
+    """The tensor's bytes, flattened (uint8)."""
     x = x.detach().contiguous()
     if x.dtype == torch.bfloat16:
         x = x.view(torch.int16)
-    return x.cpu().numpy().view(np.uint8)
+    return x.cpu().numpy().reshape(-1).view(np.uint8)
 
 
 def sample_seqs(wl, k: int, seed: int = 0):

@@ -131,7 +131,10 @@ def test_random_mixes(pa, idx):
     c = device_case(wl)
     out = run_step(pa, wl, c)
     ref, pool_ref = oracle.run_workload(wl)
-    assert np.array_equal(raw_bytes(c["pool"]), pool_ref.view(np.uint8).reshape(-1))
+    got_pool, want_pool = raw_bytes(c["pool"]), pool_ref.reshape(-1).view(np.uint8)
+    assert got_pool.shape == want_pool.shape
+    bad = np.count_nonzero(got_pool != want_pool)
+    assert bad == 0, f"{bad} pool bytes differ after the KV write"
     e = assert_within(to_f64(out), ref, wl.dtype, f"mix {idx}")
     say(f"[mix {idx}] {e}")
 
