@@ -4,9 +4,10 @@
 A step is one pa_step call over one synthetic batch: KV write through
 slot_mapping, split-K decode with partial reduce, and chunked prefill, over the
 flattened super-sequence. Inputs are generated on the device before timing
-and stay resident in HBM. Before each timed step a 2 GiB buffer is written so
+and stay resident in HBM. Before each timed step a 2 GiB buffer is read so
 that no K/V is left in the 256 MB Infinity Cache or the L2s (the TinyLlama
-batch reads only ~71 MB); the flush sits outside the per-step events.
+batch reads only ~71 MB); reading rather than writing leaves no dirty lines
+draining to HBM during the step. The flush sits outside the per-step events.
 
 Prints ONE JSON line. The headline workload is the TinyLlama-1.1B-shaped
 decode batch (64 sequences, contexts uniform in [128, 2048], 32/4 heads, head
@@ -57,7 +58,7 @@ def device_inputs(wl):
     return c
 
 
-def measure(cfg: int, steps: int, warmup: int, flush: bool = True) -> dict:
+def measure(cfg: int, steps: int, warmup: int, flush: str = "read") -> dict:
     import torch
 
     import pagedattention_block_paged_amd as pa
@@ -73,15 +74,26 @@ def measure(cfg: int, steps: int, warmup: int, flush: bool = True) -> dict:
     pool = c["pool"]
     out = torch.empty_like(c["q"])
     ws = pa.new_workspace(c["q"], pool[:, 0], c["block_tables"])
-    scratch = torch.empty(2 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    scratch = torch.ones(2 << 30, dtype=torch.uint8, device="cuda") if flush != "none" else None
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def evict(i):
+        # Read (default) or write 2 GiB so no K/V stays in the L2s or the 256 MB
+        # Infinity Cache. A read flush leaves no dirty lines draining to HBM
+        # while the next step runs.
+        if scratch is None:
+            return
+        if flush == "read":
+            torch.sum(scratch.view(torch.int64), dim=0, keepdim=True, out=sink)
+        else:
+            scratch.fill_(i & 0x7F)
 
     def one_step():
         pa.step(c["q"], c["k"], c["v"], pool[:, 0], pool[:, 1], c["slot_mapping"], c["block_tables"],
                 c["query_start_loc"], c["seq_lens"], c["context_lens"], wl.scale, out=out, workspace=ws)
 
     for i in range(warmup):
-        if scratch is not None:
-            scratch.fill_(i & 0x7F)
+        evict(i)
         one_step()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -89,8 +101,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: bool = True) -> dict:
     t_wall = time.perf_counter()
     with pa.profile() as prof:
         for i in range(steps):
-            if scratch is not None:
-                scratch.fill_(i & 0x7F)
+            evict(i)
             starts[i].record()
             one_step()
             ends[i].record()
@@ -134,6 +145,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: bool = True) -> dict:
         p = kern["prefill"]["avg_ms"]
         r["prefill_tflops"] = flops / (p * 1e-3) / 1e12
         r["prefill_mfma_frac"] = r["prefill_tflops"] / BF16_PEAK_TFLOPS
+    r["flush"] = flush
     del c, pool, out, ws, scratch
     torch.cuda.empty_cache()
     return r
@@ -181,7 +193,8 @@ def main():
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
+                    help="cache eviction between timed steps (outside the step events)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -194,14 +207,14 @@ def main():
     import pagedattention_block_paged_amd  # noqa: F401  (fails loudly if libpa.so is missing)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    head = measure(args.config, args.steps, args.warmup, flush=not args.no_flush)
+    head = measure(args.config, args.steps, args.warmup, flush=args.flush)
     log(f"[bench] headline: {json.dumps(head)}")
     secondary = {}
     if args.secondary != "none":
         for cfg in [int(x) for x in args.secondary.split(",") if x]:
             if cfg == args.config:
                 continue
-            r = measure(cfg, args.secondary_steps, 1, flush=not args.no_flush)
+            r = measure(cfg, args.secondary_steps, 1, flush=args.flush)
             log(f"[bench] cfg {cfg}: {json.dumps(r)}")
             secondary[r["workload"]] = r
     if args.calibrate_copy:

@@ -257,6 +257,9 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   a->elem = cs.dtype == PA_F32 ? pa::Elem::F32 : pa::Elem::BF16;
   a->part_tokens = pa::partition_tokens(S, cs.Hkv, MB);
   a->max_parts = (MB * pa::kBlockTokens + a->part_tokens - 1) / a->part_tokens;
+  if (MB > (int64_t(1) << 26) || a->max_parts > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "block_tables has too many columns (%lld)", (long long)MB);
+  if (S * cs.Hkv > int64_t(0x7fffffff)) return fail(PA_ERR_UNSUPPORTED, "too many sequences x KV heads");
   char* base = static_cast<char*>(ws);
   a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
   a->ws_ml = reinterpret_cast<float2*>(base + wl.ml_off);
@@ -288,15 +291,16 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
     return (v >= kBlockTokens && v % kBlockTokens == 0) ? int64_t(v) : int64_t(0);
   }();
   if (forced) return forced;
-  // Largest partition that still gives about 16 waves per CU on the
-  // longest possible sequences (256 CUs): long contexts get long partitions
-  // (fewer partial results), short batches get more parallel work.
+  // A partition is one workgroup's share of a sequence (4 waves, blocks
+  // round-robin). Take the largest partition (fewest partial results) that
+  // still yields about 2048 workgroups -- 8 waves per CU on 256 CUs -- on the
+  // longest sequences the block table allows.
   const int64_t max_len = MB * kBlockTokens;
-  for (int64_t pt : {1024, 512, 256, 128}) {
+  for (int64_t pt : {2048, 1024, 512, 256, 128, 64}) {
     const int64_t parts = (max_len + pt - 1) / pt;
-    if (S * Hkv * parts >= 4096) return pt;
+    if (S * Hkv * parts >= 2048) return pt;
   }
-  return 128;
+  return 64;
 }
 
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB) {
