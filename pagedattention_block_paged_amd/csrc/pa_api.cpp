@@ -262,6 +262,8 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   if (S * cs.Hkv > int64_t(0x7fffffff)) return fail(PA_ERR_UNSUPPORTED, "too many sequences x KV heads");
   char* base = static_cast<char*>(ws);
   a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
+  a->work_counter = reinterpret_cast<int32_t*>(base + wl.counter_off);
+  a->tile_order = reinterpret_cast<int32_t*>(base + wl.order_off);
   a->ws_ml = reinterpret_cast<float2*>(base + wl.ml_off);
   a->ws_o = reinterpret_cast<float*>(base + wl.o_off);
   return PA_OK;
@@ -310,7 +312,9 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
   const int64_t pt = partition_tokens(S, Hkv, MB);
   const int64_t parts = (MB * kBlockTokens + pt - 1) / pt;
   w.tile_start_off = 0;
-  w.ml_off = align(size_t(S + 1) * sizeof(int32_t));
+  w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
+  w.order_off = w.counter_off + 256;
+  w.ml_off = w.order_off + align(size_t(kMaxSortedTiles) * sizeof(int32_t));
   w.o_off = w.ml_off + align(size_t(S) * Hq * parts * sizeof(float2));
   w.total = w.o_off + align(size_t(S) * Hq * parts * D * sizeof(float));
   return w;

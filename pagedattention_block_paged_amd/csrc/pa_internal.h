@@ -51,11 +51,17 @@ struct AttnArgs {
   float* ws_o;          // [S][Hq][max_parts][D] unnormalised partial outputs
   float2* ws_ml;        // [S][Hq][max_parts] (running max in log2 units, sum of weights)
   // prefill work list
-  int32_t* tile_start;  // [S + 1] exclusive prefix sum of prefill q-tiles per sequence
+  int32_t* tile_start;    // [S + 1] exclusive prefix sum of prefill q-tiles per sequence
+  int32_t* tile_order;    // [kMaxSortedTiles] q-tiles by decreasing key count (if they fit)
+  int32_t* work_counter;  // prefill work-queue head, zeroed by the plan kernel
 };
 
+// Up to this many prefill q-tiles are sorted by cost (longest first) before
+// the prefill kernel takes them from a queue; beyond it they go in order.
+constexpr int kMaxSortedTiles = 4096;
+
 struct WorkspaceLayout {
-  size_t tile_start_off, ml_off, o_off, total;
+  size_t tile_start_off, counter_off, order_off, ml_off, o_off, total;
 };
 
 int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB);

@@ -7,21 +7,28 @@
 // ("Inside vLLM", section "Scheduler": prefill is usually compute-bound).
 //
 // Design for gfx950 (the pages give no kernel design):
-//  - A plan kernel lists the q-tiles of every prefill sequence (exclusive
-//    prefix sum of tiles per sequence), so the host never reads lengths.
+//  - A plan kernel lists the q-tiles of every prefill sequence, sorts them by
+//    key count (longest first, when they fit in one workgroup's sort) and
+//    resets a work-queue head, so the host never reads lengths. Workgroups
+//    take tiles from the queue until it is empty: longest-first greedy
+//    assignment keeps the 9x spread of chunk contexts from leaving a tail.
 //  - A workgroup of 4 waves owns one (q-tile, KV head, group of HW query
 //    heads); wave w takes query head hw = w % HW and 32 tokens of sub-tile
-//    w / HW. The 4 waves share K/V tiles of 64 keys staged in LDS: K row-major,
-//    V transposed ([d][key]) while staging, so both matrix-core operands are
-//    read with plain vector LDS reads.
-//  - S^T = K . Q^T with 32x32 MFMA (bf16: 32x32x16). With keys as rows, each
-//    lane owns one query token: the row max needs one cross-lane exchange, the
-//    rescale of the output accumulators needs none, and the scores are already
-//    laid out as the B operand of O^T = V^T . P^T (P rounded to bf16).
-//  - Online softmax in log2 units with the same lazy rescale as decode.
-//  - Workgroups loop over the work list; item % num_kv_heads is the KV head,
-//    so with 8 KV heads and a grid that is a multiple of 8 every XCD serves
-//    one KV head and re-reads its K/V from its own L2.
+//    w / HW. The waves share K/V tiles of 64 keys in LDS.
+//  - bf16: K and V tiles are staged row-major in LDS with a 16-byte XOR
+//    swizzle (row r, chunk c at c ^ (r mod chunks)), double buffered: the
+//    next tile's global loads are in flight while the current tile is
+//    computed, with one barrier per tile.
+//  - S^T = K . Q^T on 32x32x16 bf16 MFMA (keys as rows): each lane owns one
+//    query token, so the row max needs one cross-lane exchange and the output
+//    rescale none. The scores are already the B operand of O^T = V^T . P^T; the
+//    V^T operand comes straight from the row-major tile through gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16), two per MFMA.
+//  - Online softmax in log2 units with the scale folded into one FMA before
+//    exp2, the same lazy rescale as decode, and the causal mask only on tiles
+//    that cross the diagonal or the sequence end.
+//  - fp32 inputs take a simpler exact kernel (fp32 MFMA, V transposed while
+//    staging); it exists for accuracy, not speed.
 #include <algorithm>
 #include <type_traits>
 
@@ -32,7 +39,9 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
@@ -47,20 +56,25 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // Tokens per workgroup tile for a given number of heads per workgroup.
 constexpr int tile_tokens(int hw) { return kWaveTokens * (kWaves / hw); }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, int64_t S, int64_t T, int qtile,
-                                                    int32_t* tile_start) {
+// One block of 1024 threads: per-sequence tile counts, exclusive scan into
+// tile_start, cost-sorted tile order (if it fits), queue head reset.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const int32_t* ctx_lens,
+                                                    const int32_t* seq_lens, int64_t S, int64_t T, int64_t MB,
+                                                    int qtile, int32_t* tile_start, int32_t* tile_order,
+                                                    int32_t* counter) {
   __shared__ int32_t part[1024];
+  __shared__ uint64_t keys[kMaxSortedTiles];
   const int tid = threadIdx.x;
   const int64_t per = (S + 1023) / 1024;
   const int64_t s0 = min(S, tid * per), s1 = min(S, s0 + per);
-  auto tiles = [&](int64_t s) -> int32_t {
+  auto qlen = [&](int64_t s) -> int64_t {
     const int64_t a = min(max(static_cast<int64_t>(qsl[s]), int64_t(0)), T);
     const int64_t b = min(max(static_cast<int64_t>(qsl[s + 1]), a), T);
-    const int64_t n = b - a;
-    return n > 1 ? static_cast<int32_t>((n + qtile - 1) / qtile) : 0;
+    return b - a;
   };
+  auto tiles = [&](int64_t n) -> int32_t { return n > 1 ? static_cast<int32_t>((n + qtile - 1) / qtile) : 0; };
   int32_t sum = 0;
-  for (int64_t s = s0; s < s1; ++s) sum += tiles(s);
+  for (int64_t s = s0; s < s1; ++s) sum += tiles(qlen(s));
   part[tid] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -69,90 +83,332 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, int64_t 
     part[tid] += v;
     __syncthreads();
   }
+  const int32_t total = part[1023];
+  int len = 1;  // the sort covers the next power of two >= total
+  while (len < total) len <<= 1;
+  if (total <= kMaxSortedTiles)
+    for (int i = total + tid; i < len; i += 1024) keys[i] = 0;  // empty slots sort last
   int32_t run = part[tid] - sum;
   for (int64_t s = s0; s < s1; ++s) {
     tile_start[s] = run;
-    run += tiles(s);
+    const int64_t n = qlen(s);
+    const int32_t nt = tiles(n);
+    if (total <= kMaxSortedTiles) {
+      const int64_t C = max(static_cast<int64_t>(ctx_lens[s]), int64_t(0));
+      const int64_t Lc = min(max(static_cast<int64_t>(seq_lens[s]), int64_t(0)), MB * kBlockTokens);
+      for (int32_t lt = 0; lt < nt; ++lt) {
+        const int64_t cost = max(int64_t(0), min(C + min(n, int64_t(lt + 1) * qtile), Lc));
+        const uint32_t t = static_cast<uint32_t>(run + lt);
+        keys[t] = (static_cast<uint64_t>(cost) << 32) | (0xffffffffu - t);
+      }
+    }
+    run += nt;
   }
-  if (tid == 1023) tile_start[S] = part[1023];
+  if (tid == 1023) tile_start[S] = total;
+  if (tid == 0) *counter = 0;
+  if (total > kMaxSortedTiles) return;  // uniform: tiles go in sequence order
+  __syncthreads();
+  // bitonic sort, descending (empty slots hold key 0 and sort last)
+  for (int k = 2; k <= len; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < len; i += 1024) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = keys[i], y = keys[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? x < y : x > y) {
+            keys[i] = y;
+            keys[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < total; i += 1024) tile_order[i] = static_cast<int32_t>(0xffffffffu - uint32_t(keys[i]));
 }
 
-template <bool BF16, int D>
-struct PrefillShape {
-  static constexpr int ES = BF16 ? 2 : 4;
-  static constexpr int KT = BF16 ? 64 : 32;     // keys per LDS stage
-  static constexpr int KPAD = BF16 ? 8 : 4;     // row padding of K tile (elements)
-  static constexpr int VPAD = 4;                // row padding of V^T tile (elements)
-  static constexpr int QF = BF16 ? D / 16 : D / 2;  // Q fragments per lane
-  using E = typename std::conditional<BF16, uint16_t, float>::type;
+// Which sequence and local tile a queue item names.
+struct TileRef {
+  int64_t s, lt, g, hg;
 };
 
-template <bool BF16, int D, int HW>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(AttnArgs a) {
-  using Sh = PrefillShape<BF16, D>;
-  using E = typename Sh::E;
-  constexpr int KT = Sh::KT, ES = Sh::ES;
-  constexpr int KROW = D + Sh::KPAD;   // elements per K tile row
-  constexpr int VROW = KT + Sh::VPAD;  // elements per V^T tile row
+__device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int64_t total_tiles) {
+  TileRef r;
+  r.g = item % a.Hkv;
+  const int64_t rest = item / a.Hkv;
+  r.hg = rest % n_hg;
+  const int64_t rank = rest / n_hg;
+  const int64_t t = total_tiles <= kMaxSortedTiles ? int64_t(a.tile_order[rank]) : rank;
+  int64_t lo = 0, hi = a.S - 1;  // last s with tile_start[s] <= t
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if (a.tile_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  r.s = lo;
+  r.lt = t - a.tile_start[lo];
+  return r;
+}
+
+// Pull the next queue item for the whole workgroup.
+__device__ inline int64_t next_item(const AttnArgs& a, int* item_sh) {
+  if (threadIdx.x == 0) *item_sh = atomicAdd(a.work_counter, 1);
+  __syncthreads();
+  const int64_t item = *item_sh;
+  __syncthreads();
+  return item;
+}
+
+// ---------------------------------------------------------------- bf16 ----
+template <int D>
+struct Bf16Tile {
+  static constexpr int KT = 64;                    // keys per stage
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int CHUNKS = KT * CPR;          // per K or V tile
+  static constexpr int LOADS = CHUNKS / kThreads;  // 16-byte loads per thread per tile (K and V each)
+  __device__ static int chunk(int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); }
+};
+
+template <int D, int HW>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a) {
+  using Tl = Bf16Tile<D>;
+  constexpr int KT = Tl::KT, CPR = Tl::CPR, LOADS = Tl::LOADS;
   constexpr int QTB = tile_tokens(HW);
-  constexpr int VPR = D * ES / 16;     // 16-byte vectors per K/V row
-  __shared__ __attribute__((aligned(16))) E ks[KT * KROW];
-  __shared__ __attribute__((aligned(16))) E vt[D * VROW];
+  constexpr int QS = D / 16;  // k-steps of S^T
+  extern __shared__ uint4 lds[];  // [stage 2][K | V][CHUNKS]
+  __shared__ int item_sh;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int col = lane & 31;  // query token of this lane (B/C column)
   const int hh = lane >> 5;   // lane half
+  const int j16 = lane & 15, g16 = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = wave % HW, tw = wave / HW;
   const int G = static_cast<int>(a.Hq / a.Hkv);
   const int n_hg = G / HW;
   const int64_t total_tiles = a.tile_start[a.S];
-  const int64_t items = total_tiles * a.Hkv * n_hg;
-  const float qk_scale = a.scale * kLog2e;
+  const int64_t n_items = total_tiles * a.Hkv * n_hg;
+  const float c_scale = a.scale * kLog2e;
+  const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
 
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t g = it % a.Hkv;
-    const int64_t rest = it / a.Hkv;
-    const int64_t hg = rest % n_hg;
-    const int64_t trank = rest / n_hg;
-    // sequence owning tile `trank`: last s with tile_start[s] <= trank
-    int64_t lo = 0, hi = a.S - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) >> 1;
-      if (a.tile_start[mid] <= trank) lo = mid; else hi = mid - 1;
+  for (int64_t item = next_item(a, &item_sh); item < n_items; item = next_item(a, &item_sh)) {
+    const TileRef tr = locate(a, item, n_hg, total_tiles);
+    // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
+    const int64_t s = tr.s, g = tr.g;
+    const int lt = static_cast<int>(tr.lt), hg = static_cast<int>(tr.hg);
+    const int64_t q0 = min(max(static_cast<int64_t>(a.qsl[s]), int64_t(0)), a.T);
+    const int n = static_cast<int>(min(max(static_cast<int64_t>(a.qsl[s + 1]), q0), a.T) - q0);
+    const int Lc = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
+    const int C = min(max(a.ctx_lens[s], 0), Lc);
+    const int64_t h = g * G + hg * HW + hw;
+    const int i0 = lt * QTB + tw * kWaveTokens;  // first token of this wave
+    const bool wave_active = i0 < n;
+    const int blk_last = min(n, (lt + 1) * QTB) - 1;  // last token of the tile
+    const int kend = min(C + blk_last + 1, Lc);       // keys [0, kend) needed by the tile
+    const int wave_kend = wave_active ? min(C + min(n, i0 + kWaveTokens), Lc) : 0;
+    const int wave_first = C + i0;                    // smallest position among the wave's tokens
+    const int my_i = min(i0 + col, n - 1);            // clamped token of this lane
+    const int my_pos = C + my_i;                      // last key this lane sees
+    const int nkt = (kend + KT - 1) / KT;
+
+    bf16x8 qf[QS];  // Q^T (B operand): token col, d = 16 st + 8 hh .. +8
+    {
+      const char* qrow = a.q + (q0 + my_i) * a.q_st + h * a.q_sh + 16 * hh;
+#pragma unroll
+      for (int st = 0; st < QS; ++st)
+        qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * st));
     }
-    const int64_t s = lo;
-    const int64_t ntiles = a.tile_start[s + 1] - a.tile_start[s];
-    const int64_t lt = ntiles - 1 - (trank - a.tile_start[s]);  // heavier (later) tiles first
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int32_t* bt = a.block_tables + s * a.bt_row;
+    const char* kc = a.kc + g * a.kc_sh;
+    const char* vc = a.vc + g * a.vc_sh;
+    uint4 kreg[LOADS], vreg[LOADS];
+    auto fetch = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+        const int j = kt * KT + r;
+        kreg[i] = make_uint4(0, 0, 0, 0);
+        vreg[i] = make_uint4(0, 0, 0, 0);
+        if (j < kend) {
+          const uint32_t id32 = static_cast<uint32_t>(bt[j / kBlockTokens]);
+          const int64_t pid = id32 < NB ? int64_t(id32) : 0;
+          const int off = j % kBlockTokens;
+          kreg[i] = *reinterpret_cast<const uint4*>(kc + pid * a.kc_sb + off * a.kc_sr + 16 * c);
+          vreg[i] = *reinterpret_cast<const uint4*>(vc + pid * a.vc_sb + off * a.vc_sr + 16 * c);
+        }
+      }
+    };
+    auto stash = [&](int stage) {
+      uint4* k_l = lds + stage * 2 * Tl::CHUNKS;
+      uint4* v_l = k_l + Tl::CHUNKS;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+        k_l[Tl::chunk(r, c)] = kreg[i];
+        v_l[Tl::chunk(r, c)] = vreg[i];
+      }
+    };
+
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int stage = kt & 1;
+      if (kt + 1 < nkt) fetch(kt + 1);
+      const int k0 = kt * KT;
+      if (wave_active && k0 < wave_kend) {
+        const uint4* k_l = lds + stage * 2 * Tl::CHUNKS;
+        const char* v_b = reinterpret_cast<const char*>(k_l + Tl::CHUNKS);
+#pragma unroll 1
+        for (int half = 0; half < KT / 32; ++half) {
+          const int kh0 = k0 + 32 * half;
+          if (kh0 >= wave_kend) break;
+          f32x16 sacc;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+          const int kr = 32 * half + col;
+#pragma unroll
+          for (int st = 0; st < QS; ++st) {
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, k_l[Tl::chunk(kr, 2 * st + hh)]);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
+          }
+          // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
+          float sc[16];
+          const bool edge = (kh0 + 31 > wave_first) || (kh0 + 31 >= kend);
+          float tmax = -INFINITY;
+          if (edge) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kh0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+              sc[i] = (key <= my_pos && key < kend) ? sacc[i] : -INFINITY;
+              tmax = fmaxf(tmax, sc[i]);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              sc[i] = sacc[i];
+              tmax = fmaxf(tmax, sc[i]);
+            }
+          }
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
+          if (__any(tmax > m_run + kRescaleThreshold)) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+            m_run = m_new;
+          }
+          float pv[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+            l_run += pv[i];
+          }
+          // O^T[d][token] += V^T[d][key] P^T[key][token]; key slots of lane half hh:
+          // e < 4 -> 16 q2 + 4 hh + e, e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4)
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
+            const int kb = 32 * half + 16 * q2 + 4 * hh;  // key row of the first transposed read
+            const int r1 = kb + (j16 >> 2), r2 = r1 + 8;
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) {
+              // lane j16 of 16-lane group g16 points at V[row][d .. d + 3]; the
+              // transposing read hands it V[kb + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
+              const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
+              const int c = d >> 3, sub = (d & 7) * 2;
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_b + Tl::chunk(r1, c) * 16 + sub));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_b + Tl::chunk(r2, c) * 16 + sub));
+              const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+              const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (kt + 1 < nkt) stash(stage ^ 1);
+      __syncthreads();
+    }
+
+    if (wave_active) {
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
+      const int my_tok = i0 + col;
+      if (my_tok < n) {
+        const float inv = 1.f / l_tot;
+        char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
+        // lane holds O^T[d = 32 dt + 8 q + 4 hh + r][token col]
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d = 32 * dt + 8 * q + 4 * hh;
+            *reinterpret_cast<uint2*>(dst + 2 * d) =
+                make_uint2(pack_bf16(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv),
+                           pack_bf16(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv));
+          }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 ----
+template <int D, int HW>
+__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
+  constexpr int KT = 32;        // keys per LDS stage
+  constexpr int KROW = D + 4;   // floats per K tile row
+  constexpr int VROW = KT + 4;  // floats per V^T tile row
+  constexpr int QTB = tile_tokens(HW);
+  constexpr int VPR = D / 4;    // 16-byte vectors per K/V row
+  __shared__ __attribute__((aligned(16))) float ks[KT * KROW];
+  __shared__ __attribute__((aligned(16))) float vt[D * VROW];
+  __shared__ int item_sh;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = wave % HW, tw = wave / HW;
+  const int G = static_cast<int>(a.Hq / a.Hkv);
+  const int n_hg = G / HW;
+  const int64_t total_tiles = a.tile_start[a.S];
+  const int64_t n_items = total_tiles * a.Hkv * n_hg;
+  const float c_scale = a.scale * kLog2e;
+  const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
+
+  for (int64_t item = next_item(a, &item_sh); item < n_items; item = next_item(a, &item_sh)) {
+    const TileRef tr = locate(a, item, n_hg, total_tiles);
+    const int64_t s = tr.s, lt = tr.lt, g = tr.g, hg = tr.hg;
     const int64_t q0 = min(max(static_cast<int64_t>(a.qsl[s]), int64_t(0)), a.T);
     const int64_t n = min(max(static_cast<int64_t>(a.qsl[s + 1]), q0), a.T) - q0;
     const int64_t C = max(static_cast<int64_t>(a.ctx_lens[s]), int64_t(0));
     const int64_t Lc = min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens);
     const int64_t h = g * G + hg * HW + hw;
-    const int64_t i0 = lt * QTB + tw * kWaveTokens;  // first token of this wave
+    const int64_t i0 = lt * QTB + tw * kWaveTokens;
     const bool wave_active = i0 < n;
-    const int64_t blk_last = min(n, (lt + 1) * QTB) - 1;      // last token of the tile
-    const int64_t kend = min(C + blk_last + 1, Lc);           // keys [0, kend) needed by the tile
+    const int64_t blk_last = min(n, (lt + 1) * QTB) - 1;
+    const int64_t kend = min(C + blk_last + 1, Lc);
     const int64_t wave_kend = wave_active ? min(C + min(n, i0 + kWaveTokens), Lc) : 0;
-    const int64_t my_i = min(i0 + col, n - 1);                // clamped token of this lane
-    const int64_t my_pos = C + my_i;                          // last visible key of this lane
+    const int64_t my_i = min(i0 + col, n - 1);
+    const int64_t my_pos = C + my_i;
 
-    // Q^T fragments (B operand of S^T = K . Q^T)
-    typedef typename std::conditional<BF16, bf16x8, float>::type QFrag;
-    QFrag qf[Sh::QF];
+    float qf[D / 2];  // Q^T: token col, d = 2 st + hh
     {
-      const char* qrow = a.q + (q0 + my_i) * a.q_st + h * a.q_sh;
-      if constexpr (BF16) {
+      const float* qrow = reinterpret_cast<const float*>(a.q + (q0 + my_i) * a.q_st + h * a.q_sh);
 #pragma unroll
-        for (int st = 0; st < Sh::QF; ++st)
-          qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 2 * (16 * st + 8 * hh)));
-      } else {
-#pragma unroll
-        for (int st = 0; st < Sh::QF; ++st) qf[st] = reinterpret_cast<const float*>(qrow)[2 * st + hh];
-      }
+      for (int st = 0; st < D / 2; ++st) qf[st] = qrow[2 * st + hh];
     }
-
     f32x16 o[D / 32];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -165,168 +421,81 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(AttnArgs a) {
     const char* vc = a.vc + g * a.vc_sh;
     for (int64_t k0 = 0; k0 < kend; k0 += KT) {
       __syncthreads();  // previous tile fully consumed
-      // stage K rows [k0, k0 + KT) row-major
       for (int v = tid; v < KT * VPR; v += kThreads) {
         const int key = v / VPR, c = v % VPR;
         const int64_t j = k0 + key;
-        uint4 val = make_uint4(0, 0, 0, 0);
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
         if (j < kend) {
-          int64_t id = bt[j / kBlockTokens];
-          id = static_cast<uint64_t>(id) < static_cast<uint64_t>(a.NB) ? id : 0;
-          val = *reinterpret_cast<const uint4*>(kc + id * a.kc_sb + (j % kBlockTokens) * a.kc_sr + 16 * c);
+          const uint32_t id32 = static_cast<uint32_t>(bt[j / kBlockTokens]);
+          const int64_t pid = id32 < NB ? int64_t(id32) : 0;
+          kv = *reinterpret_cast<const float4*>(kc + pid * a.kc_sb + (j % kBlockTokens) * a.kc_sr + 16 * c);
+          vv = *reinterpret_cast<const float4*>(vc + pid * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 16 * c);
         }
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(ks) + (key * KROW) * ES + 16 * c) = val;
-      }
-      // stage V rows transposed: vt[d][key]
-      if constexpr (BF16) {
-        // pairs of keys -> 32-bit words (V[key][d], V[key + 1][d])
-        for (int v = tid; v < (KT / 2) * VPR; v += kThreads) {
-          const int kp = v / VPR, c = v % VPR;
-          uint4 r0 = make_uint4(0, 0, 0, 0), r1 = make_uint4(0, 0, 0, 0);
-          const int64_t j = k0 + 2 * kp;
-          if (j < kend) {
-            int64_t id = bt[j / kBlockTokens];
-            id = static_cast<uint64_t>(id) < static_cast<uint64_t>(a.NB) ? id : 0;
-            r0 = *reinterpret_cast<const uint4*>(vc + id * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 16 * c);
-          }
-          if (j + 1 < kend) {
-            int64_t id = bt[(j + 1) / kBlockTokens];
-            id = static_cast<uint64_t>(id) < static_cast<uint64_t>(a.NB) ? id : 0;
-            r1 = *reinterpret_cast<const uint4*>(vc + id * a.vc_sb + ((j + 1) % kBlockTokens) * a.vc_sr + 16 * c);
-          }
-          const uint32_t w0[4] = {r0.x, r0.y, r0.z, r0.w};
-          const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-          uint32_t* base = reinterpret_cast<uint32_t*>(vt);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d = 8 * c + 2 * e;
-            base[(d * VROW + 2 * kp) / 2] = (w0[e] & 0xffffu) | (w1[e] << 16);
-            base[((d + 1) * VROW + 2 * kp) / 2] = (w0[e] >> 16) | (w1[e] & 0xffff0000u);
-          }
-        }
-      } else {
-        for (int v = tid; v < KT * VPR; v += kThreads) {
-          const int key = v / VPR, c = v % VPR;
-          const int64_t j = k0 + key;
-          float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (j < kend) {
-            int64_t id = bt[j / kBlockTokens];
-            id = static_cast<uint64_t>(id) < static_cast<uint64_t>(a.NB) ? id : 0;
-            f = *reinterpret_cast<const float4*>(vc + id * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 16 * c);
-          }
-          float* base = reinterpret_cast<float*>(vt);
-          base[(4 * c + 0) * VROW + key] = f.x;
-          base[(4 * c + 1) * VROW + key] = f.y;
-          base[(4 * c + 2) * VROW + key] = f.z;
-          base[(4 * c + 3) * VROW + key] = f.w;
-        }
+        *reinterpret_cast<float4*>(ks + key * KROW + 4 * c) = kv;
+        vt[(4 * c + 0) * VROW + key] = vv.x;
+        vt[(4 * c + 1) * VROW + key] = vv.y;
+        vt[(4 * c + 2) * VROW + key] = vv.z;
+        vt[(4 * c + 3) * VROW + key] = vv.w;
       }
       __syncthreads();
-      if (!wave_active) continue;
-
+      if (!wave_active || k0 >= wave_kend) continue;
+      f32x16 sacc;
 #pragma unroll
-      for (int half = 0; half < KT / 32; ++half) {
-        const int64_t kh0 = k0 + 32 * half;
-        if (kh0 >= wave_kend) break;
-        // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
-        f32x16 sacc;
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        if constexpr (BF16) {
+      for (int st = 0; st < D / 2; ++st)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[col * KROW + 2 * st + hh], qf[st], sacc, 0, 0, 0);
+      float sc[16];
+      float tmax = -INFINITY;
 #pragma unroll
-          for (int st = 0; st < Sh::QF; ++st) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&ks[(32 * half + col) * KROW + 16 * st + 8 * hh]);
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
-          }
-        } else {
+      for (int i = 0; i < 16; ++i) {
+        const int64_t key = k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        sc[i] = (key <= my_pos && key < kend) ? sacc[i] : -INFINITY;
+        tmax = fmaxf(tmax, sc[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
+      if (__any(tmax > m_run + kRescaleThreshold)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-          for (int st = 0; st < Sh::QF; ++st) {
-            const float kf = ks[(32 * half + col) * KROW + 2 * st + hh];
-            sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[st], sacc, 0, 0, 0);
-          }
-        }
-        float sc[16];
-        float tmax = -INFINITY;
+        for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+        m_run = m_new;
+      }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = kh0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          sc[i] = (key <= my_pos && key < kend) ? sacc[i] * qk_scale : -INFINITY;
-          tmax = fmaxf(tmax, sc[i]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        if (__any(tmax > m_run + kRescaleThreshold)) {
-          const float m_new = fmaxf(m_run, tmax);
-          const float alpha = fast_exp2(m_run - m_new);
-          l_run *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+        l_run += p;
+        const int key = 8 * (i >> 2) + 4 * hh + (i & 3);
 #pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-          m_run = m_new;
-        }
-        float pv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pv[i] = fast_exp2(sc[i] - m_run);
-          l_run += pv[i];
-        }
-        // O^T[d][token] += V^T[d][key] P^T[key][token]
-        if constexpr (BF16) {
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
-            // key slots: e < 4 -> 16 q2 + 4 hh + e; e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4)
-            const int kb = 32 * half + 16 * q2 + 4 * hh;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-              const E* row = &vt[(32 * dt + col) * VROW];
-              const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
-              const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 8);
-              const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * half + 8 * (i >> 2) + 4 * hh + (i & 3);
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-              const float va = vt[(32 * dt + col) * VROW + key];
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(va, pv[i], o[dt], 0, 0, 0);
-            }
-          }
-        }
+        for (int dt = 0; dt < D / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vt[(32 * dt + col) * VROW + key], p, o[dt], 0, 0, 0);
       }
     }
 
     if (wave_active) {
-      float l_tot = l_run + __shfl_xor(l_run, 32);
+      const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int64_t my_tok = i0 + col;
       if (my_tok < n) {
         const float inv = 1.f / l_tot;
         char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
-        // lane holds O^T[d = 32 dt + 8 q + 4 hh + r][token col]
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int d = 32 * dt + 8 * q + 4 * hh;
-            if constexpr (BF16) {
-              *reinterpret_cast<uint2*>(dst + 2 * d) =
-                  make_uint2(pack_bf16(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv),
-                             pack_bf16(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv));
-            } else {
-              *reinterpret_cast<float4*>(dst + 4 * d) =
-                  make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
-                              o[dt][4 * q + 3] * inv);
-            }
+            *reinterpret_cast<float4*>(dst + 4 * d) =
+                make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
+                            o[dt][4 * q + 3] * inv);
           }
       }
     }
   }
+}
+
+template <int D>
+constexpr size_t bf16_lds_bytes() {
+  return sizeof(uint4) * 2 * 2 * Bf16Tile<D>::CHUNKS;
 }
 
 template <bool BF16, int D, int HW>
@@ -334,21 +503,27 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   constexpr int QTB = tile_tokens(HW);
   {
     ProfileScope ps(kPlan, stream);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.S, a.T, QTB, a.tile_start);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.S, a.T, a.MB,
+                       QTB, a.tile_start, a.tile_order, a.work_counter);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Upper bound on tiles without reading lengths: every prefill sequence has
+  // Upper bound on work without reading lengths: every prefill sequence has
   // at least two tokens.
   const int64_t tiles_ub = a.T / QTB + std::min<int64_t>(a.S, a.T / 2);
   const int64_t G = a.Hq / a.Hkv;
   const int64_t items_ub = tiles_ub * a.Hkv * (G / HW);
   if (items_ub == 0) return hipSuccess;
-  const int64_t grid = std::min<int64_t>((items_ub + 7) / 8 * 8, 2048);
+  const int64_t grid = std::min<int64_t>(items_ub, 1024);
   {
     ProfileScope ps(kPrefill, stream);
-    hipLaunchKernelGGL((prefill_kernel<BF16, D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
-                       a);
+    if constexpr (BF16) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                         bf16_lds_bytes<D>(), stream, a);
+    } else {
+      hipLaunchKernelGGL((prefill_f32_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                         a);
+    }
   }
   return hipGetLastError();
 }
@@ -361,9 +536,24 @@ hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
   return launch_typed<BF16, D, 1>(a, stream);
 }
 
+template <int D, int HW>
+hipError_t allow_lds() {
+  // The double-buffered bf16 tiles take 64 KB of dynamic LDS at D = 128.
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, HW>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bf16_lds_bytes<D>()));
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
+  static const hipError_t lds_ok = [] {
+    hipError_t e = hipSuccess;
+    for (hipError_t r : {allow_lds<64, 1>(), allow_lds<64, 2>(), allow_lds<64, 4>(), allow_lds<128, 1>(),
+                         allow_lds<128, 2>(), allow_lds<128, 4>()})
+      if (r != hipSuccess) e = r;
+    return e;
+  }();
+  if (lds_ok != hipSuccess) return lds_ok;
   const bool bf16 = a.elem == Elem::BF16;
   if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream) : launch_heads<false, 64>(a, stream);
   return bf16 ? launch_heads<true, 128>(a, stream) : launch_heads<false, 128>(a, stream);
