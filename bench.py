@@ -9,12 +9,15 @@ that no K/V is left in the 256 MB Infinity Cache or the L2s (the TinyLlama
 batch reads only ~71 MB); reading rather than writing leaves no dirty lines
 draining to HBM during the step. The flush sits outside the per-step events.
 
-Prints ONE JSON line. The headline workload is the TinyLlama-1.1B-shaped
-decode batch (64 sequences, contexts uniform in [128, 2048], 32/4 heads, head
-size 64, bf16); `value` is its decode KV-read bandwidth over the whole step.
-`secondary` holds the same measurement for the other model-shaped workloads:
-the Llama-3-8B mixed chunked-prefill + decode step (tokens/s, prefill
-TFLOP/s), the Llama-3-70B 32k decode and the shared-prefix decode.
+Prints ONE JSON line. The headline workload is the Llama-3-8B-shaped mixed
+step: 4096 decode tokens (contexts uniform in [256, 8192]) and 8 prefill
+chunks of 512 tokens (prior contexts uniform in [0, 4096]) in one flattened
+batch of 8192 tokens, 32/8 heads, head size 128, bf16 -- the one workload that
+runs every part of the path. `value` is its decode KV-read bandwidth over the
+whole step; the line also carries mixed-step tokens/s, prefill TFLOP/s and the
+roofline of the decode (HBM) and prefill (bf16 MFMA) kernels. `secondary`
+holds the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode and the
+shared-prefix decode.
 """
 from __future__ import annotations
 
@@ -31,7 +34,9 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read GB/s (% HBM peak), mixed-step tokens/s, prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-HEADLINE = 2
+HEADLINE = 3
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "pagedattention_block_paged_amd", "csrc")
 
 
 def log(*a):
@@ -158,36 +163,99 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read") -> dict:
     return r
 
 
+def host_inputs(wl):
+    """Host copies of one workload's inputs (numpy; bf16 as uint16 bits).
+
+    Generated on the GPU with the torch twin of the generator when one is
+    present (same bits as the numpy twin, much faster), else with numpy.
+    """
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        k, v = W.new_kv_host(wl)
+        return W.pool_host(wl), k, v, W.q_host(wl)
+
+    def h(t):
+        t = t.cpu()
+        return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+    k, v = W.new_kv_device(wl, "cuda")
+    return h(W.pool_device(wl, "cuda")), h(k), h(v), h(W.q_device(wl, "cuda"))
+
+
 def cpu_baseline(cfg: int, budget_s: float) -> dict:
-    """The oracle, as is, on the host cores: write + attention over the whole batch, repeated."""
+    """The oracle, as is, on the host cores, over a bounded sample of the workload.
+
+    Decode: a seeded sample of the workload's decode sequences (KV write +
+    attention), repeated until `budget_s` has passed; reported as decode
+    KV-read GB/s. Prefill: the workload's longest prefill chunk, once, as
+    GFLOP/s (fp64).
+    """
+    import numpy as np
+
     import oracle
     import workloads as W
 
     wl = W.config_workload(cfg)
-    pool0 = W.pool_host(wl)
-    k, v = W.new_kv_host(wl)
-    q = W.q_host(wl)
-    passes, threads, t0 = 0, 0, time.perf_counter()
-    while True:
-        pool = pool0.copy()
-        a = time.perf_counter()
-        oracle.reshape_and_cache(k, v, pool, wl.slot_mapping, wl.dtype)
-        _, threads = oracle.attention(q, pool, wl.block_tables, wl.query_start_loc, wl.seq_lens, wl.context_lens,
-                                      wl.scale, wl.dtype, return_threads=True)
-        passes += 1
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s:
-            break
-    secs = elapsed  # includes the pool copy per pass (a few ms)
-    return {
-        "value": wl.decode_bytes() * passes / secs / 1e9,
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"whole {wl.name} batch ({wl.num_seqs} sequences), KV write + attention, {passes} passes "
-                  f"in {secs:.1f} s, fp64, {threads} OpenMP threads",
-        "tokens_per_s": wl.num_tokens * passes / secs,
-    }
+    dec = np.nonzero(wl.decode_mask())[0]
+    pre = np.nonzero(~wl.decode_mask())[0]
+    rs = np.random.default_rng(7)
+    take = dec if dec.size <= 128 else np.sort(rs.choice(dec, size=128, replace=False))
+    out = {"unit": "GB/s", "kind": "oracle"}
+    if take.size:
+        sub = W.sub_workload(wl, take)
+        pool0, k, v, q = host_inputs(sub)
+        passes, threads, t0 = 0, 0, time.perf_counter()
+        while True:
+            pool = pool0.copy()
+            oracle.reshape_and_cache(k, v, pool, sub.slot_mapping, sub.dtype)
+            _, threads = oracle.attention(q, pool, sub.block_tables, sub.query_start_loc, sub.seq_lens,
+                                          sub.context_lens, sub.scale, sub.dtype, return_threads=True)
+            passes += 1
+            secs = time.perf_counter() - t0  # includes one pool copy per pass
+            if secs >= budget_s:
+                break
+        out.update({
+            "value": sub.decode_bytes() * passes / secs / 1e9,
+            "cores": threads,
+            "sample": f"{take.size} of {dec.size} decode sequences of {wl.name} (seeded), KV write + attention, "
+                      f"{passes} passes in {secs:.1f} s, fp64, {threads} OpenMP threads",
+            "decode_tokens_per_s": take.size * passes / secs,
+        })
+    if pre.size:
+        s = int(pre[np.argmax(wl.seq_lens[pre])])
+        sub = W.sub_workload(wl, [s])
+        pool, k, v, q = host_inputs(sub)
+        t0 = time.perf_counter()
+        oracle.reshape_and_cache(k, v, pool, sub.slot_mapping, sub.dtype)
+        _, threads = oracle.attention(q, pool, sub.block_tables, sub.query_start_loc, sub.seq_lens, sub.context_lens,
+                                      sub.scale, sub.dtype, return_threads=True)
+        secs = time.perf_counter() - t0
+        out["prefill_gflops"] = sub.prefill_flops() / secs / 1e9
+        out["prefill_sample"] = (f"longest prefill chunk ({int(sub.query_lens[0])} tokens after "
+                                 f"{int(sub.context_lens[0])} cached), once, {secs:.2f} s, {threads} threads")
+        out.setdefault("cores", threads)
+    return out
+
+
+def kernel_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if the kernel source is unchanged."""
+    import hashlib
+
+    path = os.path.join(PROFILES, "counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel, {}).get(workload)
+    if not rec:
+        return None
+    with open(os.path.join(CSRC, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None  # the kernel changed since the counters were taken
+    return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
 
 def main():
@@ -196,7 +264,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
-    ap.add_argument("--secondary", default="3,4,5", help="other workloads to measure, or 'none'")
+    ap.add_argument("--secondary", default="2,4,5", help="other workloads to measure, or 'none'")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -237,6 +305,7 @@ def main():
         log(f"[bench] cpu baseline: {json.dumps(cpu)}")
 
     dec = head.get("decode_kernel_gbs")
+    pre = head.get("prefill_tflops")
     line = {
         "metric": METRIC,
         "value": head["decode_gbs_step"],
@@ -261,7 +330,10 @@ def main():
             "pool_blocks": head["pool_blocks"],
             "parallelism": "single GPU",
         },
+        "value_definition": "decode KV-read bytes (K, V, block tables, q) per whole pa_step, divided by the step time",
         "hbm_frac_step": head["decode_gbs_step"] / HBM_PEAK_GBS,
+        "mixed_step_tokens_per_s": head["tokens_per_s"],
+        "prefill_tflops": pre,
         "roofline": {
             "kernel": "decode",
             "bound": "hbm",
@@ -269,7 +341,18 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": (dec / HBM_PEAK_GBS) if dec else None,
-            "traffic": None,
+            "traffic": kernel_traffic("decode", head["workload"]),
+            "algorithmic_bytes": head.get("decode_kernel_bytes"),
+        },
+        "roofline_prefill": None if pre is None else {
+            "kernel": "prefill",
+            "bound": "mfma",
+            "achieved": pre,
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": pre / BF16_PEAK_TFLOPS,
+            "traffic": kernel_traffic("prefill", head["workload"]),
+            "algorithmic_flops": head["prefill_flops"],
         },
         "cpu_baseline": cpu,
         "kernels": head["kernels"],
