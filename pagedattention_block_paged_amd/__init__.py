@@ -23,7 +23,9 @@ import os
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpa.so")
+# PA_LIBRARY names another build of the library (for side-by-side timing);
+# by default the in-package libpa.so is loaded.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(HERE, "libpa.so")
 BLOCK_SIZE = 16
 
 PA_F32, PA_BF16, PA_I32, PA_I64 = 0, 1, 2, 3

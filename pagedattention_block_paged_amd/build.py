@@ -17,6 +17,9 @@ def hipcc_command(out: str = LIB, extra=()) -> list:
         "hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep the compiler from forming packed fp32 instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in VGPRs: the softmax works on them with VALU
+        # instructions, and AGPR accumulators cost a copy each way per tile
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"),
         *extra,

@@ -2,6 +2,7 @@
 // descriptors, workspace layout, and dispatch to the HIP kernel launchers.
 // Nothing here touches device memory or synchronises the device, so every
 // validation path runs (and is tested) on a machine without a GPU.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -260,6 +261,9 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   if (MB > (int64_t(1) << 26) || a->max_parts > 65535)
     return fail(PA_ERR_UNSUPPORTED, "block_tables has too many columns (%lld)", (long long)MB);
   if (S * cs.Hkv > int64_t(0x7fffffff)) return fail(PA_ERR_UNSUPPORTED, "too many sequences x KV heads");
+  // In-block byte offsets (row within a block, head slice) are 32-bit in the kernels.
+  if (std::max(a->kc_sr, a->vc_sr) * pa::kBlockTokens + D * es > int64_t(0x7fffffff))
+    return fail(PA_ERR_UNSUPPORTED, "cache row stride too large (%lld bytes)", (long long)std::max(a->kc_sr, a->vc_sr));
   char* base = static_cast<char*>(ws);
   a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
   a->work_counter = reinterpret_cast<int32_t*>(base + wl.counter_off);

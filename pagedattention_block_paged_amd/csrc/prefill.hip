@@ -45,6 +45,9 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
+// parts: 32-bit data format, no index stride.
+constexpr int kBufferFlags = 0x00020000;
 constexpr int kWaveTokens = 32;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -154,9 +157,20 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
 __device__ inline int64_t next_item(const AttnArgs& a, int* item_sh) {
   if (threadIdx.x == 0) *item_sh = atomicAdd(a.work_counter, 1);
   __syncthreads();
-  const int64_t item = *item_sh;
+  // uniform across the workgroup: keep it (and all that derives from it) scalar
+  const int item = __builtin_amdgcn_readfirstlane(*item_sh);
   __syncthreads();
   return item;
+}
+
+// 16 bytes at byte offset off of a block's head slice. The block base is
+// wave-uniform, so the load goes through a buffer resource built in scalar
+// registers and the per-lane offset is the only vector operand; reads at or
+// past rec bytes return zero.
+__device__ inline uint4 load_row16(const char* base, uint32_t rec, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(rec), kBufferFlags);
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
 }
 
 // ---------------------------------------------------------------- bf16 ----
@@ -170,7 +184,9 @@ struct Bf16Tile {
 };
 
 template <int D, int HW>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a) {
+// block_tables comes in again as a restrict pointer: nothing in the kernel
+// writes it, so its wave-uniform entries are read with scalar loads.
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
   using Tl = Bf16Tile<D>;
   constexpr int KT = Tl::KT, CPR = Tl::CPR, LOADS = Tl::LOADS;
   constexpr int QTB = tile_tokens(HW);
@@ -226,58 +242,109 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int32_t* bt = a.block_tables + s * a.bt_row;
+    // Per-lane byte offsets of the fragments inside a 32-row slice of a tile;
+    // the swizzle term depends only on the row modulo 16, which the slice
+    // start does not change, so these hold for every slice and stage.
+    uint32_t k_rd[QS];
+#pragma unroll
+    for (int st = 0; st < QS; ++st) k_rd[st] = 16u * Tl::chunk(col, 2 * st + hh);
+    uint32_t v_rd[D / 32][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        // lane j16 of 16-lane group g16 points at V[row][d .. d + 3]; the
+        // transposing read hands it V[row0 + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
+        const int row = 4 * hh + (j16 >> 2) + 8 * w;
+        const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
+        v_rd[dt][w] = 16u * Tl::chunk(row, d >> 3) + 2u * (d & 7);
+      }
+    const int32_t* bt = bt_all + s * a.bt_row;
     const char* kc = a.kc + g * a.kc_sh;
     const char* vc = a.vc + g * a.vc_sh;
     uint4 kreg[LOADS], vreg[LOADS];
+    // Load i of a thread covers tile row r = (tid + 256 i) / CPR, chunk
+    // c = tid % CPR. A wave's rows of one load lie in a single 16-token
+    // block, so the block-table entry and the block's base address are
+    // wave-uniform (scalar); only the in-block offset is per lane, and it is
+    // the same for every tile.
+    uint32_t k_off[LOADS], v_off[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+      k_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.kc_sr + 16 * c);
+      v_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.vc_sr + 16 * c);
+    }
+    // Rows at or past kend (only in the last tile) are loaded from the last
+    // block the tile needs, so that every address is inside the pool, and
+    // are zeroed when stashed.
+    const int last_blk = (kend - 1) / kBlockTokens;
+    // bytes of one block's head slice, from its first row
+    const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + a.D * 2);
+    const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + a.D * 2);
     auto fetch = [&](int kt) {
+      uint32_t id32[LOADS];
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
-        const int j = kt * KT + r;
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-        if (j < kend) {
-          const uint32_t id32 = static_cast<uint32_t>(bt[j / kBlockTokens]);
-          const int64_t pid = id32 < NB ? int64_t(id32) : 0;
-          const int off = j % kBlockTokens;
-          kreg[i] = *reinterpret_cast<const uint4*>(kc + pid * a.kc_sb + off * a.kc_sr + 16 * c);
-          vreg[i] = *reinterpret_cast<const uint4*>(vc + pid * a.vc_sb + off * a.vc_sr + 16 * c);
-        }
+        // block of the wave's rows in load i (lane 0's row / 16; the same for every lane)
+        const int blk = kt * (KT / kBlockTokens) + ((wave * 64 + i * kThreads) / CPR) / kBlockTokens;
+        id32[i] = static_cast<uint32_t>(bt[min(blk, last_blk)]);
+      }
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int64_t pid = id32[i] < NB ? int64_t(id32[i]) : 0;
+        kreg[i] = load_row16(kc + pid * a.kc_sb, k_rec, k_off[i]);
+        vreg[i] = load_row16(vc + pid * a.vc_sb, v_rec, v_off[i]);
       }
     };
-    auto stash = [&](int stage) {
+    auto stash = [&](int stage, int kt) {
       uint4* k_l = lds + stage * 2 * Tl::CHUNKS;
       uint4* v_l = k_l + Tl::CHUNKS;
+      if ((kt + 1) * KT <= kend) {  // uniform: every row is a real key
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
-        k_l[Tl::chunk(r, c)] = kreg[i];
-        v_l[Tl::chunk(r, c)] = vreg[i];
+        for (int i = 0; i < LOADS; ++i) {
+          const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+          k_l[Tl::chunk(r, c)] = kreg[i];
+          v_l[Tl::chunk(r, c)] = vreg[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+          const bool real = kt * KT + r < kend;
+          k_l[Tl::chunk(r, c)] = real ? kreg[i] : make_uint4(0, 0, 0, 0);
+          v_l[Tl::chunk(r, c)] = real ? vreg[i] : make_uint4(0, 0, 0, 0);
+        }
       }
     };
 
     fetch(0);
-    stash(0);
+    stash(0, 0);
+    // Everything loaded so far (Q fragments, tile 0) has landed. Without this
+    // explicit wait the compiler cannot tell at the loop head and waits on the
+    // vector-memory counter inside the MFMA chain, which also stalls on the
+    // prefetch of the next tile.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nkt; ++kt) {
       const int stage = kt & 1;
       if (kt + 1 < nkt) fetch(kt + 1);
       const int k0 = kt * KT;
       if (wave_active && k0 < wave_kend) {
-        const uint4* k_l = lds + stage * 2 * Tl::CHUNKS;
-        const char* v_b = reinterpret_cast<const char*>(k_l + Tl::CHUNKS);
-#pragma unroll 1
+        const char* k_b = reinterpret_cast<const char*>(lds + stage * 2 * Tl::CHUNKS);
+        const char* v_b = k_b + 16 * Tl::CHUNKS;
+#pragma unroll
         for (int half = 0; half < KT / 32; ++half) {
           const int kh0 = k0 + 32 * half;
           if (kh0 >= wave_kend) break;
           f32x16 sacc;
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-          const int kr = 32 * half + col;
+          const char* k_h = k_b + 32 * half * CPR * 16;  // this 32-row slice of K
 #pragma unroll
           for (int st = 0; st < QS; ++st) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, k_l[Tl::chunk(kr, 2 * st + hh)]);
+            // K[kh0 + col][16 st + 8 hh .. +8]
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k_h + k_rd[st]));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
           }
           // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
@@ -320,16 +387,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a) {
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
-            const int kb = 32 * half + 16 * q2 + 4 * hh;  // key row of the first transposed read
-            const int r1 = kb + (j16 >> 2), r2 = r1 + 8;
+            // rows 32 half + 16 q2 + [4 hh, 4 hh + 4) and the same + 8
+            const char* v_q = v_b + (32 * half + 16 * q2) * CPR * 16;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-              // lane j16 of 16-lane group g16 points at V[row][d .. d + 3]; the
-              // transposing read hands it V[kb + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
-              const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
-              const int c = d >> 3, sub = (d & 7) * 2;
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_b + Tl::chunk(r1, c) * 16 + sub));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_b + Tl::chunk(r2, c) * 16 + sub));
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_q + v_rd[dt][0]));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_q + v_rd[dt][1]));
               const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
               const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
               o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
@@ -337,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a) {
           }
         }
       }
-      if (kt + 1 < nkt) stash(stage ^ 1);
+      if (kt + 1 < nkt) stash(stage ^ 1, kt + 1);
       __syncthreads();
     }
 
@@ -519,7 +582,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
       hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                         bf16_lds_bytes<D>(), stream, a);
+                         bf16_lds_bytes<D>(), stream, a, a.block_tables);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                          a);

@@ -108,7 +108,8 @@ def mixes():
     cases = []
     rs = np.random.default_rng(1234)
     shapes = [(4, 2, 64, "f32"), (8, 8, 64, "bf16"), (16, 1, 128, "bf16"), (12, 4, 128, "f32"),
-              (32, 8, 128, "bf16"), (6, 2, 64, "bf16"), (4, 4, 128, "f32"), (64, 8, 128, "bf16")]
+              (32, 8, 128, "bf16"), (6, 2, 64, "bf16"), (4, 4, 128, "f32"), (64, 8, 128, "bf16"),
+              (8, 4, 128, "bf16"), (2, 2, 128, "bf16"), (16, 2, 64, "bf16")]
     for i, (Hq, Hkv, D, dt) in enumerate(shapes):
         S = int(rs.integers(1, 7))
         ctx, ql = [], []
@@ -123,7 +124,7 @@ def mixes():
     return cases
 
 
-@pytest.mark.parametrize("idx", range(8))
+@pytest.mark.parametrize("idx", range(11))
 def test_random_mixes(pa, idx):
     wl = mixes()[idx]
     say(f"[mix {idx}] {wl.dtype} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_size} "
@@ -161,6 +162,20 @@ def test_chunked_prefill_matches_whole_prefill(pa):
     ref, _ = oracle.run_workload(whole)
     assert_within(to_f64(got), ref, "bf16", "chunked")
     assert_within(to_f64(out_whole), ref, "bf16", "whole")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(2, 2, 128), (4, 2, 128), (16, 4, 64), (16, 2, 128)])
+def test_long_prompts_span_many_query_tiles(pa, Hq, Hkv, D):
+    """Prompts of several hundred tokens (many query tiles per sequence, ragged
+    last tile) next to decode rows, for each head-group width the prefill
+    kernel instantiates (query heads per KV head 1, 2, 4 and 8)."""
+    ctx, ql = [0, 300, 45, 700, 17], [600, 333, 1, 1, 257]
+    wl = W.build_workload(f"long{Hq}x{Hkv}x{D}", "bf16", Hq, Hkv, D, ctx, ql, seed=900 + Hq + D)
+    say(f"[long] Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} q={ql}")
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    ref, _ = oracle.run_workload(wl)
+    say(f"[long] {assert_within(to_f64(out), ref, 'bf16', 'long prompts')}")
 
 
 def test_physical_permutation_is_bit_exact(pa):
