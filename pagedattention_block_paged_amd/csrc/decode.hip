@@ -41,11 +41,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
-constexpr int kVtRow = 20;                 // bf16 elements per row of a wave's V^T tile (16 keys + pad)
+constexpr size_t kDecodeMaxLds = 80 * 1024;  // dynamic LDS a decode workgroup may ask for
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -53,16 +54,30 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 }
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
+// parts: 32-bit data format, no index stride.
+constexpr int kBufferFlags = 0x00020000;
+// Cache policy of the K/V loads: non-temporal. Each K/V byte is read once per
+// step; streaming it past the caches instead of allocating it there raises
+// the sustained read rate (measured: about 7.2 vs 6.2 TB/s for a plain read).
+constexpr int kStreamPolicy = 2;
+
+// A block's head slice as a buffer resource: the base is wave-uniform, so it
+// lives in scalar registers and the loads take only a per-lane offset.
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(bytes), kBufferFlags);
+}
+
 template <int VW>
-__device__ inline void load_words(const char* p, uint32_t (&w)[VW]) {
+__device__ inline void load_words(__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t soff, uint32_t (&w)[VW]) {
   if constexpr (VW == 2) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, soff, kStreamPolicy));
     w[0] = u.x;
     w[1] = u.y;
   } else {
 #pragma unroll
     for (int i = 0; i < VW / 4; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(p + 16 * i);
+      const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * i, soff, kStreamPolicy));
       w[4 * i] = u.x;
       w[4 * i + 1] = u.y;
       w[4 * i + 2] = u.z;
@@ -78,7 +93,25 @@ struct DecodeShape {
   static constexpr int VE = D / 16;                // V elements per lane per row
   static constexpr int VW = VE * ES / 4;           // 32-bit words per lane per V row
   static constexpr int NACC = BF16 ? D / 16 : VE;  // 16x16 accumulator tiles
-  static constexpr int VT_BYTES = BF16 ? D * kVtRow * 2 : 0;  // per-wave V^T tile
+  static constexpr int LPR = D * ES / 16;          // lanes per K row when loading (16 bytes each)
+  static constexpr int RPI = 64 / LPR;             // K rows per load instruction
+  static constexpr int KT_BYTES = kBlockTokens * D * ES;  // per-wave K tile (one block)
+  static constexpr int VT_BYTES = BF16 ? kBlockTokens * D * 2 : 0;  // per-wave V tile (one block)
+  static constexpr int TILE_BYTES = KT_BYTES + VT_BYTES;
+  // K tile: row-major, chunk c of row r at c ^ swzk(r). Fragment reads (16
+  // rows at one chunk per 16 lanes) and row writes both stay one pass per 256
+  // bytes.
+  __device__ static int swzk(int r) { return LPR == 8 ? (r >> 1) & 7 : r & 15; }
+  __device__ static int kt_off(int r, int c) { return r * D * ES + 16 * (c ^ swzk(r)); }
+  // The V tile is row-major (key, d) with its 16-byte chunks permuted within
+  // each row: chunk c of row r sits at c ^ swz(r). LDS has 64 banks of 4
+  // bytes; with this permutation the transposing reads (8 rows x 2 chunks per
+  // 32 lanes) touch every bank once, and the row writes stay conflict-free
+  // at D = 128 (two rows share a pass at D = 64: 2-way on writes only).
+  __device__ static int swz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+  __device__ static int vt_off(int r, int elem) {
+    return r * D * 2 + 16 * ((elem >> 3) ^ swz(r)) + 2 * (elem & 7);
+  }
 };
 
 template <bool BF16, int D>
@@ -88,13 +121,19 @@ struct BlockRegs {
   uint32_t v[4][Sh::VW];
 };
 
+// K: load i of a lane covers row RPI i + lane / LPR, bytes k_off = 16 (lane %
+// LPR) of it (whole 128-byte lines per instruction); V: rows 4kg + j, bytes
+// v_off.
 template <bool BF16, int D>
-__device__ inline void load_block(BlockRegs<BF16, D>& r, const char* kp, const char* vp, int64_t vc_sr) {
+__device__ inline void load_block(BlockRegs<BF16, D>& r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                  uint32_t k_off, uint32_t kc_sr, uint32_t v_off, uint32_t vc_sr) {
   using Sh = DecodeShape<BF16, D>;
 #pragma unroll
-  for (int c = 0; c < Sh::KC; ++c) r.k[c] = *reinterpret_cast<const uint4*>(kp + 64 * c);
+  for (int i = 0; i < Sh::KC; ++i)
+    r.k[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, i * Sh::RPI * kc_sr, kStreamPolicy));
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load_words<Sh::VW>(vp + j * vc_sr, r.v[j]);
+  for (int j = 0; j < 4; ++j) load_words<Sh::VW>(vr, v_off, j * vc_sr, r.v[j]);
 }
 
 // Consume one block: scores, online softmax, P.V. `blk` is the block's index
@@ -105,18 +144,26 @@ __device__ inline void load_block(BlockRegs<BF16, D>& r, const char* kp, const c
 template <bool BF16, int D>
 __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[DecodeShape<BF16, D>::KC],
                                     f32x4 (&o)[DecodeShape<BF16, D>::NACC], float& m_run, float& l_run,
-                                    uint16_t* vt, int blk, int end, int kg, int n, float qk_scale) {
+                                    char* tile, int blk, int end, int lane, float qk_scale) {
   using Sh = DecodeShape<BF16, D>;
   constexpr int KC = Sh::KC, VE = Sh::VE, VW = Sh::VW;
+  const int n = lane & 15, kg = lane >> 4;
+  // Stage K row-major, then read the MFMA A fragments: lane (kg, n) takes row
+  // n, bytes 64 c + 16 kg (chunk 4c + kg) for k-step c.
+#pragma unroll
+  for (int i = 0; i < KC; ++i)
+    *reinterpret_cast<uint4*>(tile + Sh::kt_off(Sh::RPI * i + lane / Sh::LPR, lane % Sh::LPR)) = cur.k[i];
+  __builtin_amdgcn_wave_barrier();
   // scores S^T[token 4kg + r][head n]
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
+    const uint4 kc = *reinterpret_cast<const uint4*>(tile + Sh::kt_off(n, 4 * c + kg));
     if constexpr (BF16) {
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, cur.k[c]),
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc),
                                                      __builtin_bit_cast(bf16x8, qv[c]), acc, 0, 0, 0);
     } else {
-      const float4 kf = __builtin_bit_cast(float4, cur.k[c]);
+      const float4 kf = __builtin_bit_cast(float4, kc);
       const float4 qf = __builtin_bit_cast(float4, qv[c]);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qf.x, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qf.y, acc, 0, 0, 0);
@@ -164,22 +211,25 @@ __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[D
     }
   }
   if constexpr (BF16) {
-    // V^T tile: vt[d][key], keys 4kg..4kg+3 of column d in one 8-byte word.
+    // Stage the block's V rows (this lane: rows 4kg + j, elements VE n ..)
+    // and read V^T fragments back with the transposing LDS read.
+    char* vtb = tile + Sh::KT_BYTES;
 #pragma unroll
-    for (int w = 0; w < VW; ++w) {
-      const uint32_t v0 = cur.v[0][w], v1 = cur.v[1][w], v2 = cur.v[2][w], v3 = cur.v[3][w];
-      const int d = VE * n + 2 * w;
-      *reinterpret_cast<uint2*>(vt + d * kVtRow + 4 * kg) =
-          make_uint2((v0 & 0xffffu) | (v1 << 16), (v2 & 0xffffu) | (v3 << 16));
-      *reinterpret_cast<uint2*>(vt + (d + 1) * kVtRow + 4 * kg) =
-          make_uint2((v0 >> 16) | (v1 & 0xffff0000u), (v2 >> 16) | (v3 & 0xffff0000u));
+    for (int j = 0; j < 4; ++j) {
+      char* dst = vtb + Sh::vt_off(4 * kg + j, VE * n);
+      if constexpr (VW == 4)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(cur.v[j][0], cur.v[j][1], cur.v[j][2], cur.v[j][3]);
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(cur.v[j][0], cur.v[j][1]);
     }
     __builtin_amdgcn_wave_barrier();
     const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])));
 #pragma unroll
     for (int t = 0; t < Sh::NACC; ++t) {
-      const i16x4 va =
-          __builtin_bit_cast(i16x4, *reinterpret_cast<const uint2*>(vt + (16 * t + n) * kVtRow + 4 * kg));
+      // lane (kg, n) points at V[4kg + n/4][16t + 4(n%4) ..] and receives
+      // V[4kg + e][16t + n], e = 0..3: the A operand V^T[d][key] of tile t
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vtb + Sh::vt_off(4 * kg + (n >> 2), 16 * t + 4 * (n & 3))));
       o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[t], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
@@ -194,10 +244,16 @@ __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[D
   }
 }
 
-// Grid: x = sequence * Hkv + KV head, y = partition. Dynamic LDS: per-wave V^T
-// tiles during the sweep, then each wave's (max, sum, output) for the merge.
+// Workgroup: 8 waves, (sequence s, group of HW KV heads, partition p); grid
+// x = s * (Hkv / HW) + head group, y = p. Wave w serves KV head w % HW and,
+// of the partition's blocks, those with index = w / HW modulo 8 / HW. With
+// HW = 8 every wave streams one head through all blocks, so the 8 head
+// slices of each pool block (one contiguous block of all heads) are read by
+// one workgroup at the same time. Dynamic LDS: per-wave V tiles during the
+// sweep, then each wave's (max, sum, output) for the merge.
 template <bool BF16, int D, int NPF>
-__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
+                                                                int hw) {
   using Sh = DecodeShape<BF16, D>;
   constexpr int ES = Sh::ES, KC = Sh::KC, VE = Sh::VE;
   extern __shared__ float4 smem4[];
@@ -206,8 +262,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   const int n = lane & 15;   // K row (token) for the A operand; head column of scores
   const int kg = lane >> 4;  // lane group: token rows 4kg..4kg+3 of scores
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t Hkv = static_cast<uint32_t>(a.Hkv);
-  const uint32_t s = blockIdx.x / Hkv, g = blockIdx.x - s * Hkv;
+  const int wph = kDecodeWaves / hw;  // waves per KV head
+  const uint32_t n_hg = static_cast<uint32_t>(a.Hkv / hw);
+  const uint32_t s = blockIdx.x / n_hg, hg = blockIdx.x - s * n_hg;
+  const uint32_t g = hg * hw + wave % hw;
+  const int phase = wave / hw;
   const int p = blockIdx.y;
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
   if (q1 - q0 != 1 || q0 < 0 || q0 >= a.T) return;  // decode sequences only (whole workgroup)
@@ -221,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   const float qk_scale = a.scale * kLog2e;
   const int b0 = start / kBlockTokens;
   const int nblk = (end - start + kBlockTokens - 1) / kBlockTokens;
-  const int nbw = nblk > wave ? (nblk - wave + kWaves - 1) / kWaves : 0;  // blocks b0 + wave + 4i
+  const int nbw = nblk > phase ? (nblk - phase + wph - 1) / wph : 0;  // blocks b0 + phase + wph i
 
   // Q^T as the B operand: lane (kg, n) holds head n, the same d positions its
   // K chunks cover. Columns n >= G are zero.
@@ -233,16 +292,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       qv[c] = n < G ? *reinterpret_cast<const uint4*>(qrow + 64 * c) : make_uint4(0, 0, 0, 0);
   }
 
-  const int32_t* bt = a.block_tables + int64_t(s) * a.bt_row;
-  const char* kbase = a.kc + int64_t(g) * a.kc_sh + n * a.kc_sr + 16 * kg;
-  const char* vbase = a.vc + int64_t(g) * a.vc_sh + (4 * kg) * a.vc_sr + VE * ES * n;
+  const int32_t* bt = bt_all + int64_t(s) * a.bt_row;
+  const char* kbase = a.kc + int64_t(g) * a.kc_sh;
+  const char* vbase = a.vc + int64_t(g) * a.vc_sh;
+  const uint32_t k_off = static_cast<uint32_t>((lane / Sh::LPR) * a.kc_sr + 16 * (lane % Sh::LPR));
+  const uint32_t kc_sr = static_cast<uint32_t>(a.kc_sr);
+  const uint32_t v_off = static_cast<uint32_t>(4 * kg * a.vc_sr + VE * ES * n);
+  const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + D * ES);
+  const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + D * ES);
+  const uint32_t vc_sr = static_cast<uint32_t>(a.vc_sr);
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
   auto load = [&](BlockRegs<BF16, D>& r, int i) {
-    const uint32_t id = static_cast<uint32_t>(bt[b0 + wave + kWaves * i]);
+    const uint32_t id = static_cast<uint32_t>(bt[b0 + phase + wph * i]);
     const int64_t pid = id < NB ? int64_t(id) : 0;
-    load_block<BF16, D>(r, kbase + pid * a.kc_sb, vbase + pid * a.vc_sb, a.vc_sr);
+    load_block<BF16, D>(r, block_rsrc(kbase + pid * a.kc_sb, k_rec), block_rsrc(vbase + pid * a.vc_sb, v_rec), k_off,
+                        kc_sr, v_off, vc_sr);
   };
-  uint16_t* vt = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(smem) + wave * Sh::VT_BYTES);
+  char* tile = reinterpret_cast<char*>(smem) + wave * Sh::TILE_BYTES;
 
   f32x4 o[Sh::NACC];
 #pragma unroll
@@ -258,14 +324,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     for (int j = 0; j < NPF; ++j) {
       const int ib = i + j;
       if (ib < nbw) {
-        attend_block<BF16, D>(ring[j], qv, o, m_run, l_run, vt, b0 + wave + kWaves * ib, end, kg, n, qk_scale);
+        attend_block<BF16, D>(ring[j], qv, o, m_run, l_run, tile, b0 + phase + wph * ib, end, lane, qk_scale);
         if (ib + NPF < nbw) load(ring[j], ib + NPF);
       }
     }
   }
 
-  // merge the 4 waves: LDS layout [wave][m: 16][l: 16][o: G * D]
-  __syncthreads();  // V^T tiles are no longer in use
+  // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: G * D]
+  __syncthreads();  // K/V tiles are no longer in use
   const int wstride = 32 + G * D;
   float* ws = smem + wave * wstride;
   float l_tot = l_run + __shfl_xor(l_run, 16);
@@ -294,16 +360,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += kThreads) {
-    const int h = idx / (D / 4), d = 4 * (idx - h * (D / 4));
+  const int per_head = G * (D / 4);
+  for (int idx = threadIdx.x; idx < hw * per_head; idx += kDecodeThreads) {
+    const int hl = idx / per_head, rest = idx - hl * per_head;
+    const int h = rest / (D / 4), d = 4 * (rest - h * (D / 4));
     float m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, smem[w * wstride + h]);
+    for (int ph = 0; ph < wph; ++ph) m = fmaxf(m, smem[(hl + hw * ph) * wstride + h]);
     float lsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* wsw = smem + w * wstride;
+    for (int ph = 0; ph < wph; ++ph) {
+      const float* wsw = smem + (hl + hw * ph) * wstride;
       const float sw = fast_exp2(wsw[h] - m);  // 0 for a wave that saw no block
       lsum += sw * wsw[16 + h];
       const float4 x = *reinterpret_cast<const float4*>(wsw + 32 + h * D + d);
@@ -312,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       acc.z += sw * x.z;
       acc.w += sw * x.w;
     }
-    const int64_t hq = int64_t(g) * G + h;
+    const int64_t hq = int64_t(hg * hw + hl) * G + h;
     if (nparts == 1) {
       const float inv = 1.f / lsum;
       char* dst = a.out + int64_t(q0) * a.out_st + hq * a.out_sh + d * ES;
@@ -393,13 +459,21 @@ template <bool BF16, int D, int NPF>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   using Sh = DecodeShape<BF16, D>;
   const int G = static_cast<int>(a.Hq / a.Hkv);
-  const size_t merge = sizeof(float) * kWaves * (32 + G * D);
-  const size_t tiles = size_t(kWaves) * Sh::VT_BYTES;
+  const int hw = decode_heads_per_workgroup(a.Hkv);
+  const size_t merge = sizeof(float) * kDecodeWaves * (32 + G * D);
+  const size_t tiles = size_t(kDecodeWaves) * Sh::TILE_BYTES;
   const size_t lds = merge > tiles ? merge : tiles;
-  const dim3 grid(static_cast<unsigned>(a.S * a.Hkv), static_cast<unsigned>(a.max_parts));
+  const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
+  // 16 query heads per KV head at D = 128 need 65 KB for the merge.
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, NPF>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeMaxLds));
+  if (attr != hipSuccess) return attr;
+  if (lds > kDecodeMaxLds) return hipErrorInvalidValue;
   {
     ProfileScope ps(kDecode, stream);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, NPF>), grid, dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BF16, D, NPF>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
+                       hw);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;

@@ -297,14 +297,16 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
     return (v >= kBlockTokens && v % kBlockTokens == 0) ? int64_t(v) : int64_t(0);
   }();
   if (forced) return forced;
-  // A partition is one workgroup's share of a sequence (4 waves, blocks
-  // round-robin). Take the largest partition (fewest partial results) that
-  // still yields about 2048 workgroups -- 8 waves per CU on 256 CUs -- on the
-  // longest sequences the block table allows.
+  // A partition is one decode workgroup's share of a sequence: 8 waves over
+  // a group of KV heads. Take the largest partition (fewest partial results)
+  // that still yields kMinDecodeWorkgroups on the longest sequences the
+  // block table allows (2 workgroups of 8 waves fit a CU; 256 CUs).
+  constexpr int64_t kMinDecodeWorkgroups = 512;
+  const int64_t groups = S * (Hkv / decode_heads_per_workgroup(Hkv));
   const int64_t max_len = MB * kBlockTokens;
   for (int64_t pt : {2048, 1024, 512, 256, 128, 64}) {
     const int64_t parts = (max_len + pt - 1) / pt;
-    if (S * Hkv * parts >= 2048) return pt;
+    if (groups * parts >= kMinDecodeWorkgroups) return pt;
   }
   return 64;
 }

@@ -10,8 +10,17 @@
 namespace pa {
 
 constexpr int kBlockTokens = 16;  // token slots per KV block
-constexpr int kWaves = 4;         // waves per workgroup in every kernel
+constexpr int kWaves = 4;         // waves per workgroup (KV write, reduce, prefill)
 constexpr int kThreads = 64 * kWaves;
+constexpr int kDecodeWaves = 8;   // waves per decode workgroup
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
+// KV heads one decode workgroup serves: the largest power of two <= 8 that
+// divides Hkv (each head gets 8 / that many waves).
+inline int decode_heads_per_workgroup(int64_t Hkv) {
+  for (int hw : {8, 4, 2}) if (Hkv % hw == 0) return hw;
+  return 1;
+}
 
 enum class Elem : int { F32 = 0, BF16 = 1 };
 

@@ -180,7 +180,16 @@ struct Bf16Tile {
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int CHUNKS = KT * CPR;          // per K or V tile
   static constexpr int LOADS = CHUNKS / kThreads;  // 16-byte loads per thread per tile (K and V each)
-  __device__ static int chunk(int r, int c) { return r * CPR + (c ^ (r & (CPR - 1))); }
+  // Chunk c of row r sits at r * CPR + (c ^ swz(r)). LDS has 64 banks of 4
+  // bytes, so a 256-byte span is one pass. swz depends on r mod 16 only and
+  // keeps all three access patterns to one pass per 256 bytes: 16 rows read
+  // at one chunk (K fragments), 4 consecutive rows x 4 consecutive chunks
+  // (transposing V reads), and whole rows written by consecutive lanes.
+  __device__ static int swz(int r) {
+    return CPR == 16 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  __device__ static int chunk(int r, int c) { return r * CPR + (c ^ swz(r)); }
+  static_assert(CPR == 8 || CPR == 16, "head size 64 or 128");
 };
 
 template <int D, int HW>
