@@ -58,6 +58,11 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 
 // Tokens per workgroup tile for a given number of heads per workgroup.
 constexpr int tile_tokens(int hw) { return kWaveTokens * (kWaves / hw); }
+// The bf16 kernel runs 8 waves per workgroup (one workgroup per CU, two
+// waves per SIMD): twice the query rows share each staged K/V tile.
+constexpr int kPWaves = 8;
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 
 // One block of 1024 threads: per-sequence tile counts, exclusive scan into
 // tile_start, cost-sorted tile order (if it fits), queue head reset.
@@ -179,7 +184,7 @@ struct Bf16Tile {
   static constexpr int KT = 64;                    // keys per stage
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int CHUNKS = KT * CPR;          // per K or V tile
-  static constexpr int LOADS = CHUNKS / kThreads;  // 16-byte loads per thread per tile (K and V each)
+  static constexpr int LOADS = CHUNKS / kPThreads;  // 16-byte loads per thread per tile (K and V each)
   // Chunk c of row r sits at r * CPR + (c ^ swz(r)). LDS has 64 banks of 4
   // bytes, so a 256-byte span is one pass. swz depends on r mod 16 only and
   // keeps all three access patterns to one pass per 256 bytes: 16 rows read
@@ -192,13 +197,13 @@ struct Bf16Tile {
   static_assert(CPR == 8 || CPR == 16, "head size 64 or 128");
 };
 
-template <int D, int HW>
 // block_tables comes in again as a restrict pointer: nothing in the kernel
 // writes it, so its wave-uniform entries are read with scalar loads.
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
+template <int D, int HW>
+__global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
   using Tl = Bf16Tile<D>;
   constexpr int KT = Tl::KT, CPR = Tl::CPR, LOADS = Tl::LOADS;
-  constexpr int QTB = tile_tokens(HW);
+  constexpr int QTB = bf16_tile_tokens(HW);
   constexpr int QS = D / 16;  // k-steps of S^T
   extern __shared__ uint4 lds[];  // [stage 2][K | V][CHUNKS]
   __shared__ int item_sh;
@@ -280,7 +285,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a, c
     uint32_t k_off[LOADS], v_off[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+      const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
       k_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.kc_sr + 16 * c);
       v_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.vc_sr + 16 * c);
     }
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a, c
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         // block of the wave's rows in load i (lane 0's row / 16; the same for every lane)
-        const int blk = kt * (KT / kBlockTokens) + ((wave * 64 + i * kThreads) / CPR) / kBlockTokens;
+        const int blk = kt * (KT / kBlockTokens) + ((wave * 64 + i * kPThreads) / CPR) / kBlockTokens;
         id32[i] = static_cast<uint32_t>(bt[min(blk, last_blk)]);
       }
 #pragma unroll
@@ -312,14 +317,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(AttnArgs a, c
       if ((kt + 1) * KT <= kend) {  // uniform: every row is a real key
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-          const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+          const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
           k_l[Tl::chunk(r, c)] = kreg[i];
           v_l[Tl::chunk(r, c)] = vreg[i];
         }
       } else {
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-          const int id = tid + i * kThreads, r = id / CPR, c = id % CPR;
+          const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
           const bool real = kt * KT + r < kend;
           k_l[Tl::chunk(r, c)] = real ? kreg[i] : make_uint4(0, 0, 0, 0);
           v_l[Tl::chunk(r, c)] = real ? vreg[i] : make_uint4(0, 0, 0, 0);
@@ -572,7 +577,7 @@ constexpr size_t bf16_lds_bytes() {
 
 template <bool BF16, int D, int HW>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
-  constexpr int QTB = tile_tokens(HW);
+  constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
   {
     ProfileScope ps(kPlan, stream);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.S, a.T, a.MB,
@@ -586,11 +591,13 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   const int64_t G = a.Hq / a.Hkv;
   const int64_t items_ub = tiles_ub * a.Hkv * (G / HW);
   if (items_ub == 0) return hipSuccess;
-  const int64_t grid = std::min<int64_t>(items_ub, 1024);
+  // Workgroups pull items from the queue until it is empty: enough of them
+  // to fill every CU (bf16: one 8-wave workgroup per CU; fp32: four 4-wave).
+  const int64_t grid = std::min<int64_t>(items_ub, BF16 ? 512 : 1024);
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
                          bf16_lds_bytes<D>(), stream, a, a.block_tables);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
