@@ -355,12 +355,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
           const char* k_h = k_b + 32 * half * CPR * 16;  // this 32-row slice of K
+          // Raised priority while a wave feeds the matrix core: the other wave
+          // on the SIMD fills the gaps with its softmax instead of delaying
+          // the MFMA issue.
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int st = 0; st < QS; ++st) {
             // K[kh0 + col][16 st + 8 hh .. +8]
             const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k_h + k_rd[st]));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
           }
+          __builtin_amdgcn_s_setprio(0);
           // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
           float sc[16];
           const bool edge = (kh0 + 31 > wave_first) || (kh0 + 31 >= kend);
@@ -396,6 +401,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
           }
           // O^T[d][token] += V^T[d][key] P^T[key][token]; key slots of lane half hh:
           // e < 4 -> 16 q2 + 4 hh + e, e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4)
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int q2 = 0; q2 < 2; ++q2) {
             bf16x8 pb;
@@ -412,6 +418,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
               o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
             }
           }
+          __builtin_amdgcn_s_setprio(0);
         }
       }
       if (kt + 1 < nkt) stash(stage ^ 1, kt + 1);
