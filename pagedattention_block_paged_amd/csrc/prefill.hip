@@ -42,9 +42,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) const uint4 lds_u4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
+// The bf16 kernel keeps its reference maximum while a slice's weights (16
+// per lane) sum to at most 2^8; each weight is then at most 2^8 as well.
+constexpr float kRescaleBound = 256.0f;
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // parts: 32-bit data format, no index stride.
 constexpr int kBufferFlags = 0x00020000;
@@ -205,8 +209,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   constexpr int KT = Tl::KT, CPR = Tl::CPR, LOADS = Tl::LOADS;
   constexpr int QTB = bf16_tile_tokens(HW);
   constexpr int QS = D / 16;  // k-steps of S^T
-  extern __shared__ uint4 lds[];  // [stage 2][K | V][CHUNKS]
-  __shared__ int item_sh;
+  // [stage 2][K | V][CHUNKS], then the queue slot. No static LDS: the
+  // dynamic array starts at address 0, so fragment addresses are a per-lane
+  // base plus an immediate offset.
+  extern __shared__ uint4 lds[];
+  int* item_sh = reinterpret_cast<int*>(lds + 2 * 2 * Tl::CHUNKS);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,7 +229,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   const float c_scale = a.scale * kLog2e;
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
 
-  for (int64_t item = next_item(a, &item_sh); item < n_items; item = next_item(a, &item_sh)) {
+  for (int64_t item = next_item(a, item_sh); item < n_items; item = next_item(a, item_sh)) {
     const TileRef tr = locate(a, item, n_hg, total_tiles);
     // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
     const int64_t s = tr.s, g = tr.g;
@@ -259,9 +266,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
     // Per-lane byte offsets of the fragments inside a 32-row slice of a tile;
     // the swizzle term depends only on the row modulo 16, which the slice
     // start does not change, so these hold for every slice and stage.
+    // They are LDS byte addresses; the empty asm keeps each one in a register
+    // (otherwise the compiler re-adds the LDS base before every read) so the
+    // slice, stage and K/V offsets fold into the reads' immediate offsets.
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
     uint32_t k_rd[QS];
 #pragma unroll
-    for (int st = 0; st < QS; ++st) k_rd[st] = 16u * Tl::chunk(col, 2 * st + hh);
+    for (int st = 0; st < QS; ++st) {
+      k_rd[st] = lds0 + 16u * Tl::chunk(col, 2 * st + hh);
+      asm volatile("" : "+v"(k_rd[st]));
+    }
     uint32_t v_rd[D / 32][2];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
@@ -271,13 +285,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
         // transposing read hands it V[row0 + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
         const int row = 4 * hh + (j16 >> 2) + 8 * w;
         const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
-        v_rd[dt][w] = 16u * Tl::chunk(row, d >> 3) + 2u * (d & 7);
+        v_rd[dt][w] = lds0 + 16u * Tl::CHUNKS + 16u * Tl::chunk(row, d >> 3) + 2u * (d & 7);  // V follows K
+        asm volatile("" : "+v"(v_rd[dt][w]));
       }
     const int32_t* bt = bt_all + s * a.bt_row;
     const char* kc = a.kc + g * a.kc_sh;
     const char* vc = a.vc + g * a.vc_sh;
     uint4 kreg[LOADS], vreg[LOADS];
-    // Load i of a thread covers tile row r = (tid + 256 i) / CPR, chunk
+    // Load i of a thread covers tile row r = (tid + 512 i) / CPR, chunk
     // c = tid % CPR. A wave's rows of one load lie in a single 16-token
     // block, so the block-table entry and the block's base address are
     // wave-uniform (scalar); only the in-block offset is per lane, and it is
@@ -340,13 +355,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
     // prefetch of the next tile.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int stage = kt & 1;
+    // One key tile: the loads of the next tile are issued first and stashed
+    // into the other stage after this tile's MFMAs. The stage is a
+    // compile-time constant (the loop below runs tiles in pairs), so every
+    // LDS address is a per-lane base plus an immediate offset.
+    auto tile_step = [&](auto stage_c, int kt) {
+      constexpr int stage = decltype(stage_c)::value;
       if (kt + 1 < nkt) fetch(kt + 1);
       const int k0 = kt * KT;
       if (wave_active && k0 < wave_kend) {
-        const char* k_b = reinterpret_cast<const char*>(lds + stage * 2 * Tl::CHUNKS);
-        const char* v_b = k_b + 16 * Tl::CHUNKS;
+        constexpr uint32_t stage_off = stage * 2 * Tl::CHUNKS * 16;  // bytes
 #pragma unroll
         for (int half = 0; half < KT / 32; ++half) {
           const int kh0 = k0 + 32 * half;
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
           f32x16 sacc;
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-          const char* k_h = k_b + 32 * half * CPR * 16;  // this 32-row slice of K
+          const uint32_t k_h = stage_off + 32 * half * CPR * 16;  // this 32-row slice of K
           // Raised priority while a wave feeds the matrix core: the other wave
           // on the SIMD fills the gaps with its softmax instead of delaying
           // the MFMA issue.
@@ -362,43 +380,55 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 #pragma unroll
           for (int st = 0; st < QS; ++st) {
             // K[kh0 + col][16 st + 8 hh .. +8]
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(k_h + k_rd[st]));
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_h));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
           }
           __builtin_amdgcn_s_setprio(0);
           // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
           float sc[16];
-          const bool edge = (kh0 + 31 > wave_first) || (kh0 + 31 >= kend);
-          float tmax = -INFINITY;
-          if (edge) {
+          if ((kh0 + 31 > wave_first) || (kh0 + 31 >= kend)) {  // slice crosses the diagonal or the end
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = kh0 + 8 * (i >> 2) + 4 * hh + (i & 3);
               sc[i] = (key <= my_pos && key < kend) ? sacc[i] : -INFINITY;
-              tmax = fmaxf(tmax, sc[i]);
             }
           } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              sc[i] = sacc[i];
-              tmax = fmaxf(tmax, sc[i]);
-            }
+            for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
           }
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
-          if (__any(tmax > m_run + kRescaleThreshold)) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = fast_exp2(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-            m_run = m_new;
-          }
-          float pv[16];
+          // Weights against the running reference m_run. While no weight of
+          // the slice exceeds 2^8 (checked through the lane's sum, which also
+          // catches inf and NaN) the reference stands; otherwise the slice's
+          // true maximum is taken across the two lane halves of each token,
+          // the accumulators are rescaled and the weights recomputed. The
+          // first slice always takes that path (m_run starts at -inf).
+          float pv[16], lsum = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             pv[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
-            l_run += pv[i];
+            lsum += pv[i];
           }
+          if (__any(!(lsum <= kRescaleBound))) {
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
+            const float m_new = fmaxf(m_run, tmax);
+            if (m_new > m_run) {
+              const float alpha = fast_exp2(m_run - m_new);
+              l_run *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
+              m_run = m_new;
+            }
+            lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              pv[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+              lsum += pv[i];
+            }
+          }
+          l_run += lsum;
           // O^T[d][token] += V^T[d][key] P^T[key][token]; key slots of lane half hh:
           // e < 4 -> 16 q2 + 4 hh + e, e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4)
           __builtin_amdgcn_s_setprio(1);
@@ -408,11 +438,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
             // rows 32 half + 16 q2 + [4 hh, 4 hh + 4) and the same + 8
-            const char* v_q = v_b + (32 * half + 16 * q2) * CPR * 16;
+            const uint32_t v_q = stage_off + (32 * half + 16 * q2) * CPR * 16;
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_q + v_rd[dt][0]));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(v_q + v_rd[dt][1]));
+              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][0] + v_q));
+              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][1] + v_q));
               const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
               const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
               o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
@@ -423,6 +453,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
       }
       if (kt + 1 < nkt) stash(stage ^ 1, kt + 1);
       __syncthreads();
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+      tile_step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < nkt) tile_step(std::integral_constant<int, 1>{}, kt + 1);
     }
 
     if (wave_active) {
@@ -579,7 +613,7 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
 
 template <int D>
 constexpr size_t bf16_lds_bytes() {
-  return sizeof(uint4) * 2 * 2 * Bf16Tile<D>::CHUNKS;
+  return sizeof(uint4) * (2 * 2 * Bf16Tile<D>::CHUNKS + 1);
 }
 
 template <bool BF16, int D, int HW>
