@@ -377,12 +377,15 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
           // on the SIMD fills the gaps with its softmax instead of delaying
           // the MFMA issue.
           __builtin_amdgcn_s_setprio(1);
+          // All K fragments are read before the chain (K[kh0 + col][16 st +
+          // 8 hh .. +8]), so only the first MFMA waits for LDS.
+          bf16x8 kf[QS];
 #pragma unroll
-          for (int st = 0; st < QS; ++st) {
-            // K[kh0 + col][16 st + 8 hh .. +8]
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_h));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[st], sacc, 0, 0, 0);
-          }
+          for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_h));
+#pragma unroll
+          for (int st = 0; st < QS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sacc, 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // the fragment reads first,
+          __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // then the chain
           __builtin_amdgcn_s_setprio(0);
           // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
           float sc[16];
@@ -437,16 +440,21 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
-            // rows 32 half + 16 q2 + [4 hh, 4 hh + 4) and the same + 8
+            // rows 32 half + 16 q2 + [4 hh, 4 hh + 4) and the same + 8; all
+            // fragments of the 16 keys are read before their MFMAs
             const uint32_t v_q = stage_off + (32 * half + 16 * q2) * CPR * 16;
+            bf16x8 va[D / 32];
 #pragma unroll
             for (int dt = 0; dt < D / 32; ++dt) {
               const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][0] + v_q));
               const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][1] + v_q));
               const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-              const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-              o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[dt], 0, 0, 0);
+              va[dt] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
             }
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pb, o[dt], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 1);  // the reads first,
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 1);  // then the MFMAs
           }
           __builtin_amdgcn_s_setprio(0);
         }
