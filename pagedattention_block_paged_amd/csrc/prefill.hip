@@ -365,27 +365,36 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
       const int k0 = kt * KT;
       if (wave_active && k0 < wave_kend) {
         constexpr uint32_t stage_off = stage * 2 * Tl::CHUNKS * 16;  // bytes
+        // K fragments of a slice: K[32 half + col][16 st + 8 hh .. +8]. Slice
+        // 0's are read before its chain (only the first MFMA waits for LDS);
+        // slice 1's are read right after slice 0's chain and land during
+        // slice 0's softmax.
+        bf16x8 kf[QS];
 #pragma unroll
-        for (int half = 0; half < KT / 32; ++half) {
+        for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + stage_off));
+        static_assert(KT == 64, "two 32-key slices per stage");
+        auto slice = [&](auto half_c) {
+          constexpr int half = decltype(half_c)::value;
           const int kh0 = k0 + 32 * half;
-          if (kh0 >= wave_kend) break;
           f32x16 sacc;
 #pragma unroll
           for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-          const uint32_t k_h = stage_off + 32 * half * CPR * 16;  // this 32-row slice of K
           // Raised priority while a wave feeds the matrix core: the other wave
           // on the SIMD fills the gaps with its softmax instead of delaying
           // the MFMA issue.
           __builtin_amdgcn_s_setprio(1);
-          // All K fragments are read before the chain (K[kh0 + col][16 st +
-          // 8 hh .. +8]), so only the first MFMA waits for LDS.
-          bf16x8 kf[QS];
-#pragma unroll
-          for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_h));
 #pragma unroll
           for (int st = 0; st < QS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sacc, 0, 0, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // the fragment reads first,
-          __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // then the chain
+          if constexpr (half == 0) {
+            const uint32_t k_n = stage_off + 32 * CPR * 16;  // slice 1 of K
+#pragma unroll
+            for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_n));
+            __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // slice 0's reads,
+            __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // its chain,
+            __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // slice 1's reads
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // slice 1's chain
+          }
           __builtin_amdgcn_s_setprio(0);
           // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
           float sc[16];
@@ -457,7 +466,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
             __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 1);  // then the MFMAs
           }
           __builtin_amdgcn_s_setprio(0);
-        }
+        };
+        slice(std::integral_constant<int, 0>{});
+        if (k0 + 32 < wave_kend) slice(std::integral_constant<int, 1>{});
       }
       if (kt + 1 < nkt) stash(stage ^ 1, kt + 1);
       __syncthreads();
