@@ -17,7 +17,8 @@ runs every part of the path. `value` is its decode KV-read bandwidth over the
 whole step; the line also carries mixed-step tokens/s, prefill TFLOP/s and the
 roofline of the decode (HBM) and prefill (bf16 MFMA) kernels. `secondary`
 holds the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode and the
-shared-prefix decode.
+shared-prefix decode, each also timed as one HIP-graph replay per step
+(`ms_per_step_graph`).
 """
 from __future__ import annotations
 
@@ -63,7 +64,7 @@ def device_inputs(wl):
     return c
 
 
-def measure(cfg: int, steps: int, warmup: int, flush: str = "read") -> dict:
+def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool = False) -> dict:
     import torch
 
     import pagedattention_block_paged_amd as pa
@@ -121,6 +122,27 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read") -> dict:
         torch.cuda.synchronize()
     per = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     ms = sum(per) / len(per)
+    graph_ms = None
+    if graph:
+        # The same step captured once in a HIP graph and replayed (the cache
+        # flush stays eager, outside the events): what a serving loop that
+        # replays its decode step sees.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            one_step()
+        torch.cuda.synchronize()
+        gs = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            evict(i)
+            gs[i].record()
+            g.replay()
+            ge[i].record()
+        torch.cuda.synchronize()
+        graph_ms = sum(a.elapsed_time(b) for a, b in zip(gs, ge)) / steps
+        del g
     finite = bool(torch.isfinite(out.float()).all())
     kern = {k: {"avg_ms": v[0] / v[1], "launches": v[1]} for k, v in prof.kernels.items()}
     dec_bytes = wl.decode_bytes()
@@ -138,6 +160,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read") -> dict:
         "pool_blocks": wl.num_blocks,
         "partition_tokens": pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_blocks),
         "ms_per_step": ms,
+        "ms_per_step_graph": graph_ms,
         "ms_per_step_median": per[len(per) // 2],
         "ms_per_step_min": per[0],
         "wall_s_timed_region": wall,
@@ -270,6 +293,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache eviction between timed steps (outside the step events)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing of the secondary workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -289,7 +314,7 @@ def main():
         for cfg in [int(x) for x in args.secondary.split(",") if x]:
             if cfg == args.config:
                 continue
-            r = measure(cfg, args.secondary_steps, 1, flush=args.flush)
+            r = measure(cfg, args.secondary_steps, 1, flush=args.flush, graph=not args.no_graph)
             log(f"[bench] cfg {cfg}: {json.dumps(r)}")
             secondary[r["workload"]] = r
     if args.calibrate_copy:
