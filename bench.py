@@ -16,8 +16,9 @@ batch of 8192 tokens, 32/8 heads, head size 128, bf16 -- the one workload that
 runs every part of the path. `value` is its decode KV-read bandwidth over the
 whole step; the line also carries mixed-step tokens/s, prefill TFLOP/s and the
 roofline of the decode (HBM) and prefill (bf16 MFMA) kernels. `secondary`
-holds the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode and the
-shared-prefix decode, each also timed as one HIP-graph replay per step
+holds the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode, the
+shared-prefix decode and a speculative-decode verification batch (4 new
+tokens per sequence over long contexts), each also timed as one HIP-graph replay per step
 (`ms_per_step_graph`).
 """
 from __future__ import annotations
@@ -167,6 +168,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         "tokens_per_s": wl.num_tokens / (ms * 1e-3),
         "decode_bytes": dec_bytes,
         "decode_gbs_step": dec_bytes / (ms * 1e-3) / 1e9,
+        "kv_read_gbs_step": wl.kv_read_bytes() / (ms * 1e-3) / 1e9,
         "prefill_flops": flops,
         "kernels": kern,
         "output_finite": finite,
@@ -287,7 +289,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
-    ap.add_argument("--secondary", default="2,4,5", help="other workloads to measure, or 'none'")
+    ap.add_argument("--secondary", default="2,4,5,6", help="other workloads to measure, or 'none'")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -139,7 +139,9 @@ pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, 
 
 /*
  * Bytes of workspace pa_attention / pa_step need for these extents (the
- * split-K partial results of long decodes and the prefill tile list).
+ * split-K partial results, one set per new token of the sequences the decode
+ * kernel attends -- those whose query length times Hq / Hkv is at most 16 --
+ * and the prefill tile list).
  * Returns 0 for invalid extents.
  */
 size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,

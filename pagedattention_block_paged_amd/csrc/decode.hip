@@ -137,14 +137,15 @@ __device__ inline void load_block(BlockRegs<BF16, D>& r, __amdgpu_buffer_rsrc_t 
 }
 
 // Consume one block: scores, online softmax, P.V. `blk` is the block's index
-// within the sequence; rows at or past `end` are masked. Lane (kg, n) holds
+// within the sequence; rows at or past `end` (the partition's end) are
+// zeroed, and this lane's column sees keys below `lim` only. Lane (kg, n) holds
 // K row n and V rows 4kg..4kg+3 (elements VE*n..VE*n+VE-1) of the block.
 // Accumulators: bf16 path O^T[d = 16t + 4kg + r][head n] in o[t][r];
 // fp32 path O[head 4kg + r][d = VE*n + e] in o[e][r].
 template <bool BF16, int D>
 __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[DecodeShape<BF16, D>::KC],
                                     f32x4 (&o)[DecodeShape<BF16, D>::NACC], float& m_run, float& l_run,
-                                    char* tile, int blk, int end, int lane, float qk_scale) {
+                                    char* tile, int blk, int end, int lim, int lane, float qk_scale) {
   using Sh = DecodeShape<BF16, D>;
   constexpr int KC = Sh::KC, VE = Sh::VE, VW = Sh::VW;
   const int n = lane & 15, kg = lane >> 4;
@@ -174,13 +175,16 @@ __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[D
   float sc[4];
   const int tok0 = blk * kBlockTokens + 4 * kg;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < end) ? acc[r] * qk_scale : -INFINITY;
+  for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim) ? acc[r] * qk_scale : -INFINITY;
   float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  // A column can have no visible key yet (a later token of a short query in
+  // a partition that starts past its position): its maximum stays -inf and
+  // its weights and accumulators stay 0, never NaN.
   if (__any(mloc > m_run + kRescaleThreshold)) {
     const float m_new = fmaxf(m_run, mloc);
-    const float alpha = fast_exp2(m_run - m_new);
+    const float alpha = m_new == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
     l_run *= alpha;
     if constexpr (BF16) {
 #pragma unroll
@@ -196,9 +200,10 @@ __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[D
     m_run = m_new;
   }
   float pr[4];
+  const float m_ref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    pr[r] = fast_exp2(sc[r] - m_run);
+    pr[r] = fast_exp2(sc[r] - m_ref);
     l_run += pr[r];
   }
   // Rows past the sequence end carry weight 0 but arbitrary bits (0 * NaN is
@@ -269,27 +274,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   const int phase = wave / hw;
   const int p = blockIdx.y;
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
-  if (q1 - q0 != 1 || q0 < 0 || q0 >= a.T) return;  // decode sequences only (whole workgroup)
+  const int G = static_cast<int>(a.Hq / a.Hkv);
+  const int nq = q1 - q0;  // new tokens of the sequence
+  // this kernel's sequences only (whole workgroup); the rows must lie in [0, T)
+  if (!decode_path(nq, G) || q0 < 0 || q1 > a.T) return;
   const int PT = static_cast<int>(a.part_tokens);
   const int L = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
   const int start = p * PT;
   if (start >= L) return;  // whole workgroup
   const int end = min(start + PT, L);
   const int nparts = (L + PT - 1) / PT;
-  const int G = static_cast<int>(a.Hq / a.Hkv);
+  const int ncol = nq * G;  // columns (token i, head h) = i * G + h
+  // Column n is new token n / G at position C + n / G: it sees keys up to there.
+  const int C = min(max(a.ctx_lens[s], 0), L);
+  const int lim = min(end, C + n / G + 1);
   const float qk_scale = a.scale * kLog2e;
   const int b0 = start / kBlockTokens;
   const int nblk = (end - start + kBlockTokens - 1) / kBlockTokens;
   const int nbw = nblk > phase ? (nblk - phase + wph - 1) / wph : 0;  // blocks b0 + phase + wph i
 
-  // Q^T as the B operand: lane (kg, n) holds head n, the same d positions its
-  // K chunks cover. Columns n >= G are zero.
+  // Q^T as the B operand: lane (kg, n) holds column n = (token n / G, head
+  // n % G), the same d positions its K chunks cover. Columns >= ncol are zero.
   uint4 qv[KC];
   {
-    const char* qrow = a.q + int64_t(q0) * a.q_st + int64_t(g * G + n) * a.q_sh + 16 * kg;
+    const int qi = n < ncol ? n / G : 0, qh = n < ncol ? n % G : 0;
+    const char* qrow = a.q + int64_t(q0 + qi) * a.q_st + int64_t(g * G + qh) * a.q_sh + 16 * kg;
 #pragma unroll
     for (int c = 0; c < KC; ++c)
-      qv[c] = n < G ? *reinterpret_cast<const uint4*>(qrow + 64 * c) : make_uint4(0, 0, 0, 0);
+      qv[c] = n < ncol ? *reinterpret_cast<const uint4*>(qrow + 64 * c) : make_uint4(0, 0, 0, 0);
   }
 
   const int32_t* bt = bt_all + int64_t(s) * a.bt_row;
@@ -324,15 +336,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     for (int j = 0; j < NPF; ++j) {
       const int ib = i + j;
       if (ib < nbw) {
-        attend_block<BF16, D>(ring[j], qv, o, m_run, l_run, tile, b0 + phase + wph * ib, end, lane, qk_scale);
+        attend_block<BF16, D>(ring[j], qv, o, m_run, l_run, tile, b0 + phase + wph * ib, end, lim, lane,
+                              qk_scale);
         if (ib + NPF < nbw) load(ring[j], ib + NPF);
       }
     }
   }
 
-  // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: G * D]
+  // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: ncol * D]
   __syncthreads();  // K/V tiles are no longer in use
-  const int wstride = 32 + G * D;
+  const int wstride = 32 + ncol * D;
   float* ws = smem + wave * wstride;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     ws[16 + n] = l_tot;
   }
   if constexpr (BF16) {
-    if (n < G) {
+    if (n < ncol) {
 #pragma unroll
       for (int t = 0; t < Sh::NACC; ++t)
         *reinterpret_cast<float4*>(ws + 32 + n * D + 16 * t + 4 * kg) =
@@ -351,7 +364,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * kg + r;
-      if (h < G) {
+      if (h < ncol) {
 #pragma unroll
         for (int e = 0; e < VE; e += 4)
           *reinterpret_cast<float4*>(ws + 32 + h * D + VE * n + e) =
@@ -360,17 +373,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     }
   }
   __syncthreads();
-  const int per_head = G * (D / 4);
+  const int per_head = ncol * (D / 4);
   for (int idx = threadIdx.x; idx < hw * per_head; idx += kDecodeThreads) {
     const int hl = idx / per_head, rest = idx - hl * per_head;
-    const int h = rest / (D / 4), d = 4 * (rest - h * (D / 4));
+    const int h = rest / (D / 4), d = 4 * (rest - h * (D / 4));  // h: column
     float m = -INFINITY;
     for (int ph = 0; ph < wph; ++ph) m = fmaxf(m, smem[(hl + hw * ph) * wstride + h]);
     float lsum = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int ph = 0; ph < wph; ++ph) {
       const float* wsw = smem + (hl + hw * ph) * wstride;
-      const float sw = fast_exp2(wsw[h] - m);  // 0 for a wave that saw no block
+      // 0 for a wave that saw no block or no visible key of this column
+      const float sw = m == -INFINITY ? 0.f : fast_exp2(wsw[h] - m);
       lsum += sw * wsw[16 + h];
       const float4 x = *reinterpret_cast<const float4*>(wsw + 32 + h * D + d);
       acc.x += sw * x.x;
@@ -378,10 +392,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
       acc.z += sw * x.z;
       acc.w += sw * x.w;
     }
-    const int64_t hq = int64_t(hg * hw + hl) * G + h;
+    const int64_t hq = int64_t(hg * hw + hl) * G + h % G;
+    const int64_t t = q0 + h / G;  // the column's token
     if (nparts == 1) {
       const float inv = 1.f / lsum;
-      char* dst = a.out + int64_t(q0) * a.out_st + hq * a.out_sh + d * ES;
+      char* dst = a.out + t * a.out_st + hq * a.out_sh + d * ES;
       if constexpr (BF16) {
         *reinterpret_cast<uint2*>(dst) =
             make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
@@ -389,15 +404,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
         *reinterpret_cast<float4*>(dst) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
       }
     } else {
-      const int64_t slot = (int64_t(s) * a.Hq + hq) * a.max_parts + p;
+      const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
       *reinterpret_cast<float4*>(a.ws_o + slot * D + d) = acc;
       if (d == 0) a.ws_ml[slot] = make_float2(m, lsum);
     }
   }
 }
 
-// Combine the partitions of multi-partition decode sequences: one wave per
-// (sequence, query head), fixed partition order.
+// Combine the partitions of multi-partition sequences of the decode kernel:
+// one wave per (sequence, query head), for each of the sequence's new tokens,
+// in fixed partition order.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(AttnArgs a) {
   constexpr int DPL = D / 64;  // output elements per lane
@@ -407,60 +423,61 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(AttnArgs a) {
   const int64_t s = item / a.Hq, hq = item - s * a.Hq;
   if (s >= a.S) return;
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
-  if (q1 - q0 != 1 || q0 < 0 || q0 >= a.T) return;
+  if (!decode_path(q1 - q0, a.Hq / a.Hkv) || q0 < 0 || q1 > a.T) return;
   const int64_t L = min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens);
   const int nparts = static_cast<int>((L + a.part_tokens - 1) / a.part_tokens);
   if (nparts <= 1) return;
-  const float2* ml = a.ws_ml + (s * a.Hq + hq) * a.max_parts;
-  const float* po = a.ws_o + (s * a.Hq + hq) * a.max_parts * D + DPL * lane;
-  float m = -INFINITY;
-  for (int p = lane; p < nparts; p += 64) m = fmaxf(m, ml[p].x);
+  for (int64_t t = q0; t < q1; ++t) {
+    const float2* ml = a.ws_ml + (t * a.Hq + hq) * a.max_parts;
+    const float* po = a.ws_o + (t * a.Hq + hq) * a.max_parts * D + DPL * lane;
+    float m = -INFINITY;
+    for (int p = lane; p < nparts; p += 64) m = fmaxf(m, ml[p].x);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float acc[DPL] = {};
-  float lsum = 0.f;
-  for (int p0 = 0; p0 < nparts; p0 += 64) {
-    float w = 0.f;
-    if (p0 + lane < nparts) {
-      const float2 v = ml[p0 + lane];
-      w = fast_exp2(v.x - m);
-      lsum += w * v.y;
-    }
-    const int cnt = min(64, nparts - p0);
-    for (int j = 0; j < cnt; ++j) {
-      const float wj = __shfl(w, j);
-      const float* x = po + int64_t(p0 + j) * D;
-      if constexpr (DPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(x);
-        acc[0] += wj * v.x;
-        acc[1] += wj * v.y;
-      } else {
-        acc[0] += wj * x[0];
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float acc[DPL] = {};
+    float lsum = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += 64) {
+      float w = 0.f;
+      if (p0 + lane < nparts) {
+        const float2 v = ml[p0 + lane];
+        w = fast_exp2(v.x - m);
+        lsum += w * v.y;
+      }
+      const int cnt = min(64, nparts - p0);
+      for (int j = 0; j < cnt; ++j) {
+        const float wj = __shfl(w, j);
+        const float* x = po + int64_t(p0 + j) * D;
+        if constexpr (DPL == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(x);
+          acc[0] += wj * v.x;
+          acc[1] += wj * v.y;
+        } else {
+          acc[0] += wj * x[0];
+        }
       }
     }
-  }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-  const float inv = 1.f / lsum;
-  char* dst = a.out + q0 * a.out_st + hq * a.out_sh;
-  if constexpr (BF16) {
-    if constexpr (DPL == 2) {
-      *reinterpret_cast<uint32_t*>(dst + 4 * lane) = pack_bf16(acc[0] * inv, acc[1] * inv);
+    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
+    const float inv = 1.f / lsum;
+    char* dst = a.out + t * a.out_st + hq * a.out_sh;
+    if constexpr (BF16) {
+      if constexpr (DPL == 2) {
+        *reinterpret_cast<uint32_t*>(dst + 4 * lane) = pack_bf16(acc[0] * inv, acc[1] * inv);
+      } else {
+        reinterpret_cast<__bf16*>(dst)[lane] = static_cast<__bf16>(acc[0] * inv);
+      }
     } else {
-      reinterpret_cast<__bf16*>(dst)[lane] = static_cast<__bf16>(acc[0] * inv);
-    }
-  } else {
 #pragma unroll
-    for (int i = 0; i < DPL; ++i) reinterpret_cast<float*>(dst)[DPL * lane + i] = acc[i] * inv;
+      for (int i = 0; i < DPL; ++i) reinterpret_cast<float*>(dst)[DPL * lane + i] = acc[i] * inv;
+    }
   }
 }
 
 template <bool BF16, int D, int NPF>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   using Sh = DecodeShape<BF16, D>;
-  const int G = static_cast<int>(a.Hq / a.Hkv);
   const int hw = decode_heads_per_workgroup(a.Hkv);
-  const size_t merge = sizeof(float) * kDecodeWaves * (32 + G * D);
+  const size_t merge = sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D);  // up to 16 columns
   const size_t tiles = size_t(kDecodeWaves) * Sh::TILE_BYTES;
   const size_t lds = merge > tiles ? merge : tiles;
   const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));

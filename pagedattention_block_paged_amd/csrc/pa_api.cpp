@@ -312,7 +312,6 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
 }
 
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB) {
-  (void)T;
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w{};
   const int64_t pt = partition_tokens(S, Hkv, MB);
@@ -321,8 +320,10 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
   w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
   w.order_off = w.counter_off + 256;
   w.ml_off = w.order_off + align(size_t(kMaxSortedTiles) * sizeof(int32_t));
-  w.o_off = w.ml_off + align(size_t(S) * Hq * parts * sizeof(float2));
-  w.total = w.o_off + align(size_t(S) * Hq * parts * D * sizeof(float));
+  // split-K partials, one set per (new token, query head, partition) of the
+  // decode kernel's sequences
+  w.o_off = w.ml_off + align(size_t(T) * Hq * parts * sizeof(float2));
+  w.total = w.o_off + align(size_t(T) * Hq * parts * D * sizeof(float));
   return w;
 }
 

@@ -15,6 +15,14 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kDecodeWaves = 8;   // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
+// The decode kernel's MFMA tiles have 16 columns: (new token, query head)
+// pairs of one KV head. A sequence whose n new tokens times G query heads fit
+// them (every decode, and short chunks such as speculative-decode
+// verification) is attended by the decode kernel, with a causal limit per
+// column; longer chunks go to the prefill kernel.
+constexpr int kMaxDecodeColumns = 16;
+__host__ __device__ inline bool decode_path(int64_t n, int64_t G) { return n >= 1 && n * G <= kMaxDecodeColumns; }
+
 // KV heads one decode workgroup serves: the largest power of two <= 8 that
 // divides Hkv (each head gets 8 / that many waves).
 inline int decode_heads_per_workgroup(int64_t Hkv) {

@@ -72,7 +72,7 @@ constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 // tile_start, cost-sorted tile order (if it fits), queue head reset.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const int32_t* ctx_lens,
                                                     const int32_t* seq_lens, int64_t S, int64_t T, int64_t MB,
-                                                    int qtile, int32_t* tile_start, int32_t* tile_order,
+                                                    int64_t G, int qtile, int32_t* tile_start, int32_t* tile_order,
                                                     int32_t* counter) {
   __shared__ int32_t part[1024];
   __shared__ uint64_t keys[kMaxSortedTiles];
@@ -84,7 +84,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
     const int64_t b = min(max(static_cast<int64_t>(qsl[s + 1]), a), T);
     return b - a;
   };
-  auto tiles = [&](int64_t n) -> int32_t { return n > 1 ? static_cast<int32_t>((n + qtile - 1) / qtile) : 0; };
+  // sequences on the decode kernel's path get no prefill tiles
+  auto tiles = [&](int64_t n) -> int32_t {
+    return n >= 1 && !decode_path(n, G) ? static_cast<int32_t>((n + qtile - 1) / qtile) : 0;
+  };
   int32_t sum = 0;
   for (int64_t s = s0; s < s1; ++s) sum += tiles(qlen(s));
   part[tid] = sum;
@@ -641,14 +644,14 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   {
     ProfileScope ps(kPlan, stream);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.S, a.T, a.MB,
-                       QTB, a.tile_start, a.tile_order, a.work_counter);
+                       a.Hq / a.Hkv, QTB, a.tile_start, a.tile_order, a.work_counter);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Upper bound on work without reading lengths: every prefill sequence has
-  // at least two tokens.
-  const int64_t tiles_ub = a.T / QTB + std::min<int64_t>(a.S, a.T / 2);
+  // more than 16 / G tokens.
   const int64_t G = a.Hq / a.Hkv;
+  const int64_t tiles_ub = a.T / QTB + std::min<int64_t>(a.S, a.T / (kMaxDecodeColumns / G + 1));
   const int64_t items_ub = tiles_ub * a.Hkv * (G / HW);
   if (items_ub == 0) return hipSuccess;
   // Workgroups pull items from the queue until it is empty: enough of them

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Bounds: KV write bit-exact; fp32 max abs <= 1e-5; bf16 max abs <= 2e-2, mean
-abs <= 1e-2 and per-row max|err| <= 3e-2 * rms (tests/parity.py). The five
+abs <= 1e-2 and per-row max|err| <= 3e-2 * rms (tests/parity.py). The six
 model-shaped workloads run at full size in the launch configuration the
 benchmark times; the oracle checks every row for the small ones and a sample
 of whole sequences (always the longest and shortest) for the large ones.
@@ -61,7 +61,7 @@ def oracle_rows(wl, seqs):
     return out
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_config_parity(pa, cfg):
     wl = W.config_workload(cfg, hbm_bytes=hbm_bytes())
     say(f"[cfg {cfg}] {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
@@ -236,6 +236,27 @@ def test_split_partition_boundaries(pa, delta):
     out = run_step(pa, wl, c)
     ref, _ = oracle.run_workload(wl)
     assert_within(to_f64(out), ref, "bf16", f"split {pt}+{delta}")
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(32, 8, 128, "bf16"), (64, 8, 128, "bf16"), (8, 8, 64, "bf16"),
+                                              (16, 8, 64, "bf16"), (12, 4, 128, "f32")])
+def test_short_queries_over_long_contexts(pa, Hq, Hkv, D, dtype):
+    """Speculative-decode verification shapes: a few new tokens (every
+    n with n x G <= 16 goes to the decode kernel, one column per (token,
+    head)) after long cached contexts split into several partitions, next to
+    plain decodes and one chunk long enough for the prefill kernel."""
+    G = Hq // Hkv
+    nmax = 16 // G
+    ns = sorted({2, min(3, nmax), nmax, max(2, nmax // 2)})
+    ns = [n for n in ns if n <= nmax and n >= 2] or [1]
+    ctx = [4999, 2100, 64, 0] + [1500 + 700 * i for i in range(len(ns))] + [300]
+    ql = [1, 1, 1, nmax] + ns + [nmax + 5]
+    wl = W.build_workload(f"spec{Hq}x{Hkv}x{D}", dtype, Hq, Hkv, D, ctx, ql, seed=700 + Hq + D)
+    say(f"[spec] {dtype} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} q={ql} partition={pa.partition_tokens(wl.num_seqs, Hkv, wl.max_blocks)}")
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    ref, _ = oracle.run_workload(wl)
+    say(f"[spec] {assert_within(to_f64(out), ref, dtype, 'short queries')}")
 
 
 def test_empty_batch_is_a_no_op(pa):

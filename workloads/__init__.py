@@ -220,13 +220,17 @@ CONFIG_NAMES = {
     3: "llama3_8b_mixed_prefill_decode_bf16",
     4: "llama3_70b_32k_decode_bf16",
     5: "prefix_shared_decode_bf16",
+    6: "llama3_8b_spec_verify_bf16",
 }
 
 DEFAULT_HBM_BYTES = 288 * (1 << 30)
 
 
 def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
-    """The five benchmark/parity workloads (decode lengths include the new token)."""
+    """The benchmark/parity workloads (decode lengths include the new token).
+
+    1-5 are the path's configurations; 6 is speculative-decode verification
+    (short multi-token queries over long contexts)."""
     name = CONFIG_NAMES[cfg]
     r = _draw_rng(cfg, 0)
     if cfg == 1:
@@ -252,6 +256,12 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
         L = 2048 + p + 1
         return build_workload(name, "bf16", 32, 8, 128, L - 1, np.ones(256, np.int64), seed=cfg,
                               shared_prefix_tokens=2048, max_blocks=128 + -(-513 // BLOCK_SIZE))
+    if cfg == 6:
+        # speculative-decode verification: 3 draft tokens + 1 per sequence
+        # (n = 4 new tokens), long cached contexts, Llama-3-8B heads
+        C = r.integers(1024, 8192, size=256, endpoint=True)
+        return build_workload(name, "bf16", 32, 8, 128, C, np.full(256, 4, np.int64), seed=cfg,
+                              max_blocks=(8192 + 4) // BLOCK_SIZE + 1)
     raise ValueError(f"unknown config {cfg}")
 
 
