@@ -417,12 +417,18 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
           // true maximum is taken across the two lane halves of each token,
           // the accumulators are rescaled and the weights recomputed. The
           // first slice always takes that path (m_run starts at -inf).
-          float pv[16], lsum = 0.f;
+          // four partial sums: the adds do not form one serial chain
+          auto weights = [&](float (&w)[16]) {
+            float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            pv[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
-            lsum += pv[i];
-          }
+            for (int i = 0; i < 16; ++i) {
+              w[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+              part[i & 3] += w[i];
+            }
+            return (part[0] + part[1]) + (part[2] + part[3]);
+          };
+          float pv[16];
+          float lsum = weights(pv);
           if (__any(!(lsum <= kRescaleBound))) {
             float tmax = -INFINITY;
 #pragma unroll
@@ -436,12 +442,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
               for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
               m_run = m_new;
             }
-            lsum = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              pv[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
-              lsum += pv[i];
-            }
+            lsum = weights(pv);
           }
           l_run += lsum;
           // O^T[d][token] += V^T[d][key] P^T[key][token]; key slots of lane half hh:
