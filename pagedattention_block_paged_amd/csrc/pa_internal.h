@@ -69,7 +69,7 @@ struct AttnArgs {
   float2* ws_ml;        // [S][Hq][max_parts] (running max in log2 units, sum of weights)
   // prefill work list
   int32_t* tile_start;    // [S + 1] exclusive prefix sum of prefill q-tiles per sequence
-  int32_t* tile_order;    // [kMaxSortedTiles] q-tiles by decreasing key count (if they fit)
+  int32_t* tile_order;    // [kMaxSortedTiles][2] (sequence, tile) of the q-tiles by decreasing key count (if they fit)
   int32_t* work_counter;  // prefill work-queue head, zeroed by the plan kernel
 };
 

@@ -8,25 +8,31 @@
 //
 // Design for gfx950 (the pages give no kernel design):
 //  - A plan kernel lists the q-tiles of every prefill sequence, sorts them by
-//    key count (longest first, when they fit in one workgroup's sort) and
-//    resets a work-queue head, so the host never reads lengths. Workgroups
-//    take tiles from the queue until it is empty: longest-first greedy
-//    assignment keeps the 9x spread of chunk contexts from leaving a tail.
-//  - A workgroup of 4 waves owns one (q-tile, KV head, group of HW query
-//    heads); wave w takes query head hw = w % HW and 32 tokens of sub-tile
-//    w / HW. The waves share K/V tiles of 64 keys in LDS.
-//  - bf16: K and V tiles are staged row-major in LDS with a 16-byte XOR
-//    swizzle (row r, chunk c at c ^ (r mod chunks)), double buffered: the
-//    next tile's global loads are in flight while the current tile is
-//    computed, with one barrier per tile.
+//    key count (longest first, when they fit in one workgroup's sort),
+//    records each rank's (sequence, tile) and resets a work-queue head, so
+//    the host never reads lengths. Workgroups take tiles from the queue until
+//    it is empty: longest-first greedy assignment keeps the 9x spread of
+//    chunk contexts from leaving a tail.
+//  - bf16: one workgroup of 8 waves per CU (two per SIMD) owns one (q-tile,
+//    KV head, group of HW query heads); wave w takes query head w % HW and
+//    32 tokens of sub-tile w / HW. The waves share K/V tiles of 64 keys.
+//  - K and V tiles go from HBM straight into LDS (buffer loads that write
+//    LDS), four stages deep: a tile is requested two tiles before its use and
+//    no registers hold data in flight. Rows are stored with a 16-byte XOR
+//    swizzle that keeps both fragment read patterns free of bank conflicts.
 //  - S^T = K . Q^T on 32x32x16 bf16 MFMA (keys as rows): each lane owns one
 //    query token, so the row max needs one cross-lane exchange and the output
 //    rescale none. The scores are already the B operand of O^T = V^T . P^T; the
 //    V^T operand comes straight from the row-major tile through gfx950's
 //    transposing LDS read (ds_read_b64_tr_b16), two per MFMA.
+//  - Each wave runs a software pipeline over 32-key slices: step j computes
+//    the weights of slice j while its MFMAs are the score chain of slice
+//    j + 1 and P.V of slice j - 1. The MFMAs go out one at a time between
+//    shares of the vector work, dependent chain MFMAs alternating with
+//    independent P.V ones, and fragment reads run a few MFMAs ahead.
 //  - Online softmax in log2 units with the scale folded into one FMA before
-//    exp2, the same lazy rescale as decode, and the causal mask only on tiles
-//    that cross the diagonal or the sequence end.
+//    exp2, the same lazy rescale as decode, and the causal mask only on
+//    slices that cross the wave's diagonal.
 //  - fp32 inputs take a simpler exact kernel (fp32 MFMA, V transposed while
 //    staging); it exists for accuracy, not speed.
 #include <algorithm>
@@ -76,6 +82,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
                                                     int32_t* counter) {
   __shared__ int32_t part[1024];
   __shared__ uint64_t keys[kMaxSortedTiles];
+  __shared__ int32_t tile_seq[kMaxSortedTiles];  // sequence of each tile (sorted case)
   const int tid = threadIdx.x;
   const int64_t per = (S + 1023) / 1024;
   const int64_t s0 = min(S, tid * per), s1 = min(S, s0 + per);
@@ -115,6 +122,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
         const int64_t cost = max(int64_t(0), min(C + min(n, int64_t(lt + 1) * qtile), Lc));
         const uint32_t t = static_cast<uint32_t>(run + lt);
         keys[t] = (static_cast<uint64_t>(cost) << 32) | (0xffffffffu - t);
+        tile_seq[t] = static_cast<int32_t>(s);
       }
     }
     run += nt;
@@ -140,7 +148,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
       __syncthreads();
     }
   }
-  for (int i = tid; i < total; i += 1024) tile_order[i] = static_cast<int32_t>(0xffffffffu - uint32_t(keys[i]));
+  // (sequence, local tile) by rank, so that workgroups need no search
+  for (int i = tid; i < total; i += 1024) {
+    const int32_t t = static_cast<int32_t>(0xffffffffu - uint32_t(keys[i]));
+    const int32_t sq = tile_seq[t];
+    tile_order[2 * i] = sq;
+    tile_order[2 * i + 1] = t - tile_start[sq];
+  }
 }
 
 // Which sequence and local tile a queue item names.
@@ -154,7 +168,12 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
   const int64_t rest = item / a.Hkv;
   r.hg = rest % n_hg;
   const int64_t rank = rest / n_hg;
-  const int64_t t = total_tiles <= kMaxSortedTiles ? int64_t(a.tile_order[rank]) : rank;
+  if (total_tiles <= kMaxSortedTiles) {  // the plan kernel listed (sequence, tile) by rank
+    r.s = a.tile_order[2 * rank];
+    r.lt = a.tile_order[2 * rank + 1];
+    return r;
+  }
+  const int64_t t = rank;
   int64_t lo = 0, hi = a.S - 1;  // last s with tile_start[s] <= t
   while (lo < hi) {
     const int64_t mid = (lo + hi + 1) >> 1;
@@ -186,37 +205,86 @@ __device__ inline uint4 load_row16(const char* base, uint32_t rec, uint32_t off)
 }
 
 // ---------------------------------------------------------------- bf16 ----
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <int D>
 struct Bf16Tile {
-  static constexpr int KT = 64;                    // keys per stage
-  static constexpr int CPR = D / 8;                // 16-byte chunks per row
-  static constexpr int CHUNKS = KT * CPR;          // per K or V tile
-  static constexpr int LOADS = CHUNKS / kPThreads;  // 16-byte loads per thread per tile (K and V each)
+  static constexpr int KT = 64;                        // keys per tile
+  static constexpr int STAGES = 4;                     // LDS stages, for K and for V
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int CHUNKS = KT * CPR;              // per K or V tile
+  static constexpr uint32_t TB = CHUNKS * 16;          // bytes of one K or V tile
+  static constexpr uint32_t HALF = TB / 2;             // bytes of a 32-key slice
+  static constexpr uint32_t V0 = STAGES * TB;          // the V stages follow the K stages
+  static constexpr int DPW = CHUNKS / (64 * kPWaves);  // LDS loads per wave per K (or V) tile
   // Chunk c of row r sits at r * CPR + (c ^ swz(r)). LDS has 64 banks of 4
   // bytes, so a 256-byte span is one pass. swz depends on r mod 16 only and
-  // keeps all three access patterns to one pass per 256 bytes: 16 rows read
-  // at one chunk (K fragments), 4 consecutive rows x 4 consecutive chunks
-  // (transposing V reads), and whole rows written by consecutive lanes.
+  // keeps the two read patterns at one pass per 256 bytes: 16 rows read at
+  // one chunk (K fragments) and 4 consecutive rows x 4 consecutive chunks
+  // (transposing V reads).
   __device__ static int swz(int r) {
     return CPR == 16 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
   }
   __device__ static int chunk(int r, int c) { return r * CPR + (c ^ swz(r)); }
   static_assert(CPR == 8 || CPR == 16, "head size 64 or 128");
+  static_assert(DPW >= 1 && (64 / CPR) <= kBlockTokens, "one load instruction stays inside one cache block");
 };
 
-// block_tables comes in again as a restrict pointer: nothing in the kernel
-// writes it, so its wave-uniform entries are read with scalar loads.
+template <int D>
+constexpr size_t bf16_lds_bytes() {
+  return 2 * Bf16Tile<D>::STAGES * Bf16Tile<D>::TB + 16;  // K and V stages, then the queue slot
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 l (dst is wave-uniform); reads at or past rec bytes deliver zeros.
+__device__ inline void load_lds16(const char* base, uint32_t rec, uint32_t off, lds_char* dst) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(rec), kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(dst), 16, off, 0, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (s_waitcnt with the export and LDS counts left open).
+// The memory clobber keeps the compiler from moving loads across the wait.
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier with no wait of its own. The memory clobber keeps the
+// compiler from moving LDS accesses across it; the caller waits for what
+// must have landed.
+__device__ inline void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// f(integral_constant<int, i>) for i = I .. N - 1, unrolled at compile time.
+template <int I, int N, class F>
+__device__ __attribute__((always_inline)) inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// One queue item after another. dma and rd are two views of the same LDS:
+// the tile loads write through dma, the fragment reads go through rd. Between
+// two barriers a stage is either being loaded or being read, never both, so
+// the two kinds of access are independent; handing the compiler two distinct
+// restrict pointers lets it see that (otherwise it waits for every load in
+// flight before each LDS read).
 template <int D, int HW>
-__global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
+__device__ __attribute__((always_inline)) inline void prefill_bf16_items(const AttnArgs& a,
+                                                                        const int32_t* __restrict__ bt_all,
+                                                                        lds_char* __restrict__ dma,
+                                                                        const lds_char* __restrict__ rd,
+                                                                        int* item_sh) {
   using Tl = Bf16Tile<D>;
-  constexpr int KT = Tl::KT, CPR = Tl::CPR, LOADS = Tl::LOADS;
+  constexpr int KT = Tl::KT, CPR = Tl::CPR, DPW = Tl::DPW;
+  constexpr uint32_t TB = Tl::TB, HALF = Tl::HALF, V0 = Tl::V0;
   constexpr int QTB = bf16_tile_tokens(HW);
-  constexpr int QS = D / 16;  // k-steps of S^T
-  // [stage 2][K | V][CHUNKS], then the queue slot. No static LDS: the
-  // dynamic array starts at address 0, so fragment addresses are a per-lane
-  // base plus an immediate offset.
-  extern __shared__ uint4 lds[];
-  int* item_sh = reinterpret_cast<int*>(lds + 2 * 2 * Tl::CHUNKS);
+  constexpr int QS = D / 16;   // k-steps of S^T
+  constexpr int DT = D / 32;   // 32-row tiles of O^T
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,6 +300,44 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   const float c_scale = a.scale * kLog2e;
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
 
+  // Per-lane fragment addresses in stage 0 (K: slice 0; V: rows of slice 0).
+  // The swizzle term depends only on the row modulo 16, which no slice or
+  // stage offset changes, so these hold everywhere; the empty asm keeps each
+  // in a register so that stage and slice offsets fold into the reads'
+  // immediate offsets.
+  uint32_t k_rd[QS];
+#pragma unroll
+  for (int st = 0; st < QS; ++st) {
+    k_rd[st] = 16u * Tl::chunk(col, 2 * st + hh);
+    asm volatile("" : "+v"(k_rd[st]));
+  }
+  uint32_t v_rd[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      // lane j16 of 16-lane group g16 points at V[row][d .. d + 3]; the
+      // transposing read hands it V[row0 + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
+      const int row = 4 * hh + (j16 >> 2) + 8 * w;
+      const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
+      v_rd[dt][w] = V0 + 16u * Tl::chunk(row, d >> 3) + 2u * (d & 7);
+      asm volatile("" : "+v"(v_rd[dt][w]));
+    }
+  // Tile loads: load i of this wave fills LDS chunks [64 (wave + 8 i), +64)
+  // of a K (or V) tile; lane l fills chunk slot p = (64 (wave + 8 i) + l) mod
+  // CPR of row r, i.e. it fetches the row's logical chunk p ^ swz(r). The
+  // rows of one load lie in one 16-token block (blk_of), so the block and
+  // its address are wave-uniform; only the in-block offset is per lane.
+  uint32_t dk[DPW], dv[DPW];
+  auto row_of = [&](int i) { return 64 * (wave + kPWaves * i) / CPR + lane / CPR; };  // tile row of lane's chunk
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int r = row_of(i), c = (lane % CPR) ^ Tl::swz(r);
+    dk[i] = static_cast<uint32_t>((r % kBlockTokens) * a.kc_sr + 16 * c);
+    dv[i] = static_cast<uint32_t>((r % kBlockTokens) * a.vc_sr + 16 * c);
+  }
+  auto blk_of = [&](int i) { return (64 * (wave + kPWaves * i) / CPR) / kBlockTokens; };
+
   for (int64_t item = next_item(a, item_sh); item < n_items; item = next_item(a, item_sh)) {
     const TileRef tr = locate(a, item, n_hg, total_tiles);
     // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
@@ -246,11 +352,38 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
     const bool wave_active = i0 < n;
     const int blk_last = min(n, (lt + 1) * QTB) - 1;  // last token of the tile
     const int kend = min(C + blk_last + 1, Lc);       // keys [0, kend) needed by the tile
-    const int wave_kend = wave_active ? min(C + min(n, i0 + kWaveTokens), Lc) : 0;
-    const int wave_first = C + i0;                    // smallest position among the wave's tokens
+    const int wave_first = C + min(i0, n - 1);        // smallest position among the wave's lanes
     const int my_i = min(i0 + col, n - 1);            // clamped token of this lane
     const int my_pos = C + my_i;                      // last key this lane sees
     const int nkt = (kend + KT - 1) / KT;
+
+    const int32_t* bt = bt_all + s * a.bt_row;
+    const char* kc = a.kc + g * a.kc_sh;
+    const char* vc = a.vc + g * a.vc_sh;
+    const int last_blk = (kend - 1) / kBlockTokens;
+    // bytes of one block's head slice, from its first row
+    const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + a.D * 2);
+    const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + a.D * 2);
+    int32_t ids[DPW];  // block ids of the next tile to load (scalar)
+    auto load_ids = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) ids[i] = bt[min(t * (KT / kBlockTokens) + blk_of(i), last_blk)];
+    };
+    // Rows at or past kend (only in the last tile) read past the resource and
+    // land as zeros; their block index is clamped to a block the tile needs.
+    auto load_tile = [&](int t, uint32_t stage_off) {
+      const bool last = t == nkt - 1;
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const uint32_t u = static_cast<uint32_t>(ids[i]);
+        const int64_t pid = u < NB ? int64_t(u) : 0;
+        uint32_t ok = dk[i], ov = dv[i];
+        if (last && t * KT + row_of(i) >= kend) ok = ov = 0x80000000u;
+        lds_char* dst = dma + stage_off + 1024u * (wave + kPWaves * i);
+        load_lds16(kc + pid * a.kc_sb, k_rec, ok, dst);
+        load_lds16(vc + pid * a.vc_sb, v_rec, ov, dst + V0);
+      }
+    };
 
     bf16x8 qf[QS];  // Q^T (B operand): token col, d = 16 st + 8 hh .. +8
     {
@@ -259,227 +392,313 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
       for (int st = 0; st < QS; ++st)
         qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * st));
     }
-    f32x16 o[D / 32];
+    f32x16 o[DT];
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Per-lane byte offsets of the fragments inside a 32-row slice of a tile;
-    // the swizzle term depends only on the row modulo 16, which the slice
-    // start does not change, so these hold for every slice and stage.
-    // They are LDS byte addresses; the empty asm keeps each one in a register
-    // (otherwise the compiler re-adds the LDS base before every read) so the
-    // slice, stage and K/V offsets fold into the reads' immediate offsets.
-    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
-    uint32_t k_rd[QS];
-#pragma unroll
-    for (int st = 0; st < QS; ++st) {
-      k_rd[st] = lds0 + 16u * Tl::chunk(col, 2 * st + hh);
-      asm volatile("" : "+v"(k_rd[st]));
-    }
-    uint32_t v_rd[D / 32][2];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        // lane j16 of 16-lane group g16 points at V[row][d .. d + 3]; the
-        // transposing read hands it V[row0 + e][32 dt + 16 (g16 & 1) + j16], e = 0..3
-        const int row = 4 * hh + (j16 >> 2) + 8 * w;
-        const int d = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3);
-        v_rd[dt][w] = lds0 + 16u * Tl::CHUNKS + 16u * Tl::chunk(row, d >> 3) + 2u * (d & 7);  // V follows K
-        asm volatile("" : "+v"(v_rd[dt][w]));
-      }
-    const int32_t* bt = bt_all + s * a.bt_row;
-    const char* kc = a.kc + g * a.kc_sh;
-    const char* vc = a.vc + g * a.vc_sh;
-    uint4 kreg[LOADS], vreg[LOADS];
-    // Load i of a thread covers tile row r = (tid + 512 i) / CPR, chunk
-    // c = tid % CPR. A wave's rows of one load lie in a single 16-token
-    // block, so the block-table entry and the block's base address are
-    // wave-uniform (scalar); only the in-block offset is per lane, and it is
-    // the same for every tile.
-    uint32_t k_off[LOADS], v_off[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
-      k_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.kc_sr + 16 * c);
-      v_off[i] = static_cast<uint32_t>((r % kBlockTokens) * a.vc_sr + 16 * c);
-    }
-    // Rows at or past kend (only in the last tile) are loaded from the last
-    // block the tile needs, so that every address is inside the pool, and
-    // are zeroed when stashed.
-    const int last_blk = (kend - 1) / kBlockTokens;
-    // bytes of one block's head slice, from its first row
-    const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + a.D * 2);
-    const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + a.D * 2);
-    auto fetch = [&](int kt) {
-      uint32_t id32[LOADS];
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        // block of the wave's rows in load i (lane 0's row / 16; the same for every lane)
-        const int blk = kt * (KT / kBlockTokens) + ((wave * 64 + i * kPThreads) / CPR) / kBlockTokens;
-        id32[i] = static_cast<uint32_t>(bt[min(blk, last_blk)]);
-      }
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int64_t pid = id32[i] < NB ? int64_t(id32[i]) : 0;
-        kreg[i] = load_row16(kc + pid * a.kc_sb, k_rec, k_off[i]);
-        vreg[i] = load_row16(vc + pid * a.vc_sb, v_rec, v_off[i]);
-      }
+    // Software pipeline over 32-key slices j: step j runs the softmax of
+    // slice j, the score chain of slice j + 1 and P.V of slice j - 1, so the
+    // matrix core has independent work while the vector ALU computes weights.
+    f32x16 s_cur;     // S^T[key 32 j + 8 q + 4 hh + r][token col] in s_cur[4 q + r]
+    bf16x8 p_prev[2];  // weights of slice j - 1, the two B operands of its P.V
+    auto read_k = [&](uint32_t ko, int st) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<lds_u4*>(rd + k_rd[st] + ko));
     };
-    auto stash = [&](int stage, int kt) {
-      uint4* k_l = lds + stage * 2 * Tl::CHUNKS;
-      uint4* v_l = k_l + Tl::CHUNKS;
-      if ((kt + 1) * KT <= kend) {  // uniform: every row is a real key
+    auto read_v = [&](uint32_t vo, int q2, int dt) {
+      // rows 16 q2 + [4 hh, 4 hh + 4) and the same + 8 of the slice at vo
+      const uint32_t off = vo + 16u * q2 * CPR * 16;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_i16x4*>(const_cast<lds_char*>(rd + v_rd[dt][0] + off)));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<lds_i16x4*>(const_cast<lds_char*>(rd + v_rd[dt][1] + off)));
+      const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
+      return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+    };
+    // Weights against the running reference m_run; four partial sums keep
+    // the adds from forming one serial chain.
+    auto weights = [&](const float (&sc)[16], float (&w)[16]) {
+      float part[4];
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
-          k_l[Tl::chunk(r, c)] = kreg[i];
-          v_l[Tl::chunk(r, c)] = vreg[i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-          const int id = tid + i * kPThreads, r = id / CPR, c = id % CPR;
-          const bool real = kt * KT + r < kend;
-          k_l[Tl::chunk(r, c)] = real ? kreg[i] : make_uint4(0, 0, 0, 0);
-          v_l[Tl::chunk(r, c)] = real ? vreg[i] : make_uint4(0, 0, 0, 0);
-        }
+      for (int i = 0; i < 16; ++i) {
+        w[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+        part[i & 3] = i < 4 ? w[i] : part[i & 3] + w[i];
       }
+      return (part[0] + part[1]) + (part[2] + part[3]);
+    };
+    // key slots of lane half hh in P^T: e < 4 -> 16 q2 + 4 hh + e,
+    // e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4), i.e. w[8 q2 + e]
+    auto pack = [&](const float (&w)[16], bf16x8 (&p)[2]) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[q2][e] = static_cast<__bf16>(w[8 * q2 + e]);
+    };
+    // The reference stands while no weight of the slice exceeds 2^8 (checked
+    // through the lane's sum, which also catches inf and NaN). Otherwise the
+    // slice's true maximum is taken across the two lane halves of each token,
+    // the accumulators (which already hold P.V of the previous slice) are
+    // rescaled and the weights recomputed. The first slice always lands here
+    // (m_run starts at -inf).
+    auto settle = [&](const float (&sc)[16], float (&w)[16], float& lsum, bf16x8 (&p)[2]) {
+      if (__any(!(lsum <= kRescaleBound))) {
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
+        const float m_new = fmaxf(m_run, tmax);
+        if (m_new > m_run) {
+          const float alpha = fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+          m_run = m_new;
+        }
+        lsum = weights(sc, w);
+        pack(w, p);
+      }
+      l_run += lsum;
     };
 
-    fetch(0);
-    stash(0, 0);
-    // Everything loaded so far (Q fragments, tile 0) has landed. Without this
-    // explicit wait the compiler cannot tell at the loop head and waits on the
-    // vector-memory counter inside the MFMA chain, which also stalls on the
-    // prefetch of the next tile.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // One key tile: the loads of the next tile are issued first and stashed
-    // into the other stage after this tile's MFMAs. The stage is a
-    // compile-time constant (the loop below runs tiles in pairs), so every
-    // LDS address is a per-lane base plus an immediate offset.
-    auto tile_step = [&](auto stage_c, int kt) {
-      constexpr int stage = decltype(stage_c)::value;
-      if (kt + 1 < nkt) fetch(kt + 1);
-      const int k0 = kt * KT;
-      if (wave_active && k0 < wave_kend) {
-        constexpr uint32_t stage_off = stage * 2 * Tl::CHUNKS * 16;  // bytes
-        // K fragments of a slice: K[32 half + col][16 st + 8 hh .. +8]. Slice
-        // 0's are read before its chain (only the first MFMA waits for LDS);
-        // slice 1's are read right after slice 0's chain and land during
-        // slice 0's softmax.
-        bf16x8 kf[QS];
+    // Keys above the lane's own position (including every key at or past
+    // kend, which lies above every position) get -inf in s_cur.
+    auto mask_cur = [&](int j) {
+      const int t = my_pos - 32 * j - 4 * hh;
 #pragma unroll
-        for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + stage_off));
-        static_assert(KT == 64, "two 32-key slices per stage");
-        auto slice = [&](auto half_c) {
-          constexpr int half = decltype(half_c)::value;
-          const int kh0 = k0 + 32 * half;
-          f32x16 sacc;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-          // Raised priority while a wave feeds the matrix core: the other wave
-          // on the SIMD fills the gaps with its softmax instead of delaying
-          // the MFMA issue.
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int st = 0; st < QS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sacc, 0, 0, 0);
-          if constexpr (half == 0) {
-            const uint32_t k_n = stage_off + 32 * CPR * 16;  // slice 1 of K
-#pragma unroll
-            for (int st = 0; st < QS; ++st) kf[st] = __builtin_bit_cast(bf16x8, *(lds_u4*)(uintptr_t)(k_rd[st] + k_n));
-            __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // slice 0's reads,
-            __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // its chain,
-            __builtin_amdgcn_sched_group_barrier(0x100, QS, 0);  // slice 1's reads
-          } else {
-            __builtin_amdgcn_sched_group_barrier(0x008, QS, 0);  // slice 1's chain
-          }
-          __builtin_amdgcn_s_setprio(0);
-          // S^T[key kh0 + 8q + 4hh + r][token col] in sacc[4q + r]
-          float sc[16];
-          if ((kh0 + 31 > wave_first) || (kh0 + 31 >= kend)) {  // slice crosses the diagonal or the end
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kh0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              sc[i] = (key <= my_pos && key < kend) ? sacc[i] : -INFINITY;
-            }
-          } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sc[i] = sacc[i];
-          }
-          // Weights against the running reference m_run. While no weight of
-          // the slice exceeds 2^8 (checked through the lane's sum, which also
-          // catches inf and NaN) the reference stands; otherwise the slice's
-          // true maximum is taken across the two lane halves of each token,
-          // the accumulators are rescaled and the weights recomputed. The
-          // first slice always takes that path (m_run starts at -inf).
-          // four partial sums: the adds do not form one serial chain
-          auto weights = [&](float (&w)[16]) {
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              w[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
-              part[i & 3] += w[i];
-            }
-            return (part[0] + part[1]) + (part[2] + part[3]);
-          };
-          float pv[16];
-          float lsum = weights(pv);
-          if (__any(!(lsum <= kRescaleBound))) {
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
-            const float m_new = fmaxf(m_run, tmax);
-            if (m_new > m_run) {
-              const float alpha = fast_exp2(m_run - m_new);
-              l_run *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < D / 32; ++dt) o[dt] *= alpha;
-              m_run = m_new;
-            }
-            lsum = weights(pv);
-          }
-          l_run += lsum;
-          // O^T[d][token] += V^T[d][key] P^T[key][token]; key slots of lane half hh:
-          // e < 4 -> 16 q2 + 4 hh + e, e >= 4 -> 16 q2 + 8 + 4 hh + (e - 4)
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[8 * q2 + e]);
-            // rows 32 half + 16 q2 + [4 hh, 4 hh + 4) and the same + 8; all
-            // fragments of the 16 keys are read before their MFMAs
-            const uint32_t v_q = stage_off + (32 * half + 16 * q2) * CPR * 16;
-            bf16x8 va[D / 32];
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) {
-              const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][0] + v_q));
-              const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)(v_rd[dt][1] + v_q));
-              const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
-              va[dt] = __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
-            }
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], pb, o[dt], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 1);  // the reads first,
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 32, 1);  // then the MFMAs
-          }
-          __builtin_amdgcn_s_setprio(0);
-        };
-        slice(std::integral_constant<int, 0>{});
-        if (k0 + 32 < wave_kend) slice(std::integral_constant<int, 1>{});
-      }
-      if (kt + 1 < nkt) stash(stage ^ 1, kt + 1);
-      __syncthreads();
+      for (int i = 0; i < 16; ++i) s_cur[i] = 8 * (i >> 2) + (i & 3) <= t ? s_cur[i] : -INFINITY;
     };
-    for (int kt = 0; kt < nkt; kt += 2) {
-      tile_step(std::integral_constant<int, 0>{}, kt);
-      if (kt + 1 < nkt) tile_step(std::integral_constant<int, 1>{}, kt + 1);
+    // Step j: softmax of slice j, with P.V of slice j - 1 (PV) and the score
+    // chain of slice j + 1 (QK). Every wave runs every slice of the tile's
+    // keys; keys a lane must not see are masked, so slices past a wave's
+    // last token cost work but change nothing (their weights are zero and
+    // their V rows finite: real keys, or zeros past kend).
+    auto step = [&](auto pv_c, auto qk_c, int j, uint32_t ko, uint32_t vo) {
+      constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+      if (32 * j + 31 > wave_first) mask_cur(j);
+      // Two phases, each reading half of the fragments (V rows of one
+      // 16-key group, half of the K k-steps) before its MFMAs.
+      bf16x8 va[2][DT], kf[QS];
+      float sc[16], w[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = s_cur[i];
+      if constexpr (PV) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) va[0][dt] = read_v(vo, 0, dt);
+      }
+      if constexpr (QK) {
+#pragma unroll
+        for (int st = 0; st < QS / 2; ++st) kf[st] = read_k(ko, st);
+      }
+      float lsum = weights(sc, w);
+      bf16x8 p[2];
+      pack(w, p);
+      if constexpr (PV) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][dt], p_prev[0], o[dt], 0, 0, 0);
+      }
+      f32x16 sn;
+      if constexpr (QK) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sn[i] = 0.f;
+#pragma unroll
+        for (int st = 0; st < QS / 2; ++st) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sn, 0, 0, 0);
+      }
+      if constexpr (PV) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) va[1][dt] = read_v(vo, 1, dt);
+      }
+      if constexpr (QK) {
+#pragma unroll
+        for (int st = QS / 2; st < QS; ++st) kf[st] = read_k(ko, st);
+      }
+      if constexpr (PV) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][dt], p_prev[1], o[dt], 0, 0, 0);
+      }
+      if constexpr (QK) {
+#pragma unroll
+        for (int st = QS / 2; st < QS; ++st) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sn, 0, 0, 0);
+      }
+      if constexpr (PV && QK) {
+        // Issue order: phase 1's reads, some weights while they land, its
+        // MFMAs one at a time with weight math between them; then phase 2.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT + QS / 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+#pragma unroll
+        for (int k = 0; k < DT + QS / 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT + QS / 2, 0);
+#pragma unroll
+        for (int k = 0; k < DT + QS / 2; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
+      settle(sc, w, lsum, p);
+      p_prev[0] = p[0];
+      p_prev[1] = p[1];
+      if constexpr (QK) s_cur = sn;
+    };
+    // The steady step, scheduled by hand: the MFMAs go out one at a time,
+    // each followed by a share of the softmax's vector work (weights, their
+    // sum, the bf16 packing), and each half of the fragment reads goes out
+    // ahead of the MFMAs that use it. Scheduling fences hold that order; left
+    // alone, the compiler bunches the vector work ahead of the first MFMA.
+    auto step_steady = [&](int j, uint32_t ko, uint32_t vo) {
+      if (32 * j + 31 > wave_first) mask_cur(j);
+      constexpr int M = 2 * DT + QS;  // MFMAs
+      // Vector work items. Item k < 20 runs three independent operations:
+      // the scaled score of element k, exp2 of element k - 2 and the partial
+      // sum of element k - 4, so that no operation waits on the one before
+      // it. Then the total (item 20) and the eight bf16 pairs (21 .. 28).
+      constexpr int NW = 20 + 1 + 8;
+      float sc[16], t[16], w[16], part[4], lsum = 0.f;
+      bf16x8 p[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[i] = s_cur[i];
+      auto work = [&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        if constexpr (k < 20) {
+          if constexpr (k < 16) t[k] = __builtin_fmaf(sc[k], c_scale, -m_run);
+          if constexpr (k >= 2 && k < 18) w[k - 2] = fast_exp2(t[k - 2]);
+          if constexpr (k >= 4 && k < 8) part[k - 4] = w[k - 4];
+          if constexpr (k >= 8) part[(k - 4) & 3] += w[k - 4];
+        } else if constexpr (k == 20) {
+          lsum = (part[0] + part[1]) + (part[2] + part[3]);
+        } else {
+          constexpr int e = k - 21;  // weights 2e, 2e + 1 -> P^T slots of p[e / 4]
+          p[e / 4][2 * (e % 4)] = static_cast<__bf16>(w[2 * e]);
+          p[e / 4][2 * (e % 4) + 1] = static_cast<__bf16>(w[2 * e + 1]);
+        }
+      };
+      auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+      // MFMA m of the step: even m is k-step m / 2 of the score chain, odd m
+      // is P.V tile i = (m - 1) / 2 (16-key group i / DT, rows 32 (i % DT)).
+      // The chain's dependent MFMAs thus alternate with independent ones,
+      // which keeps the matrix core busy from this wave alone (a dependent
+      // MFMA waits for its predecessor's result, longer than the issue
+      // interval). Each fragment is read L MFMAs ahead of its use.
+      constexpr int L = 5;
+      static_assert(QS == 2 * DT, "score and P.V MFMAs alternate one for one");
+      bf16x8 fr[M];
+      auto issue_read = [&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m % 2 == 0) {
+          fr[m] = read_k(ko, m / 2);
+        } else {
+          constexpr int i = (m - 1) / 2;
+          fr[m] = read_v(vo, i / DT, i % DT);
+        }
+      };
+      static_for<0, L>(issue_read);
+      fence();
+      static_for<0, 4>(work);  // while the reads land
+      fence();
+      f32x16 sn;
+      static_for<0, M>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        if constexpr (m % 2 == 0) {
+          constexpr int st = m / 2;
+          if constexpr (st == 0) {
+            const f32x16 zero = {};
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[0], zero, 0, 0, 0);
+          } else {
+            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[st], sn, 0, 0, 0);
+          }
+        } else {
+          constexpr int i = (m - 1) / 2, q2 = i / DT, dt = i % DT;
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], p_prev[q2], o[dt], 0, 0, 0);
+        }
+        if constexpr (m + L < M) issue_read(std::integral_constant<int, m + L>{});
+        // this MFMA's share of the remaining work items 4 .. NW - 1
+        static_for<4 + (NW - 4) * m / M, 4 + (NW - 4) * (m + 1) / M>(work);
+        fence();
+      });
+      settle(sc, w, lsum, p);
+      p_prev[0] = p[0];
+      p_prev[1] = p[1];
+      s_cur = sn;
+    };
+    // The score chain of slice 0 alone, and P.V of the last slice alone.
+    auto qk_only = [&](uint32_t ko) {
+      bf16x8 kf[QS];
+#pragma unroll
+      for (int st = 0; st < QS; ++st) kf[st] = read_k(ko, st);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s_cur[i] = 0.f;
+#pragma unroll
+      for (int st = 0; st < QS; ++st) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s_cur, 0, 0, 0);
+    };
+    auto pv_only = [&](uint32_t vo) {
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2) {
+        bf16x8 va[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) va[dt] = read_v(vo, q2, dt);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], p_prev[q2], o[dt], 0, 0, 0);
+      }
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+
+    if (nkt > 0) {
+      // Prologue: tiles 0 and 1 in flight, wait for tile 0 (and the Q loads).
+      load_ids(0);
+      load_tile(0, 0);
+      if (nkt > 1) {
+        load_ids(1);
+        load_tile(1, TB);
+        wait_vmem<2 * DPW>();
+      } else {
+        wait_vmem<0>();
+      }
+      raw_barrier();
+      if (nkt > 2) {
+        load_ids(2);
+        load_tile(2, 2 * TB);
+      }
+      if (nkt > 3) load_ids(3);
+      // The Q loads have landed (they were issued before tile 0). Passing the
+      // fragments through an empty asm tells the compiler so; otherwise it
+      // cannot prove it inside the tile loop and waits there on the vector-
+      // memory count, which would also wait for the tile loads in flight.
+#pragma unroll
+      for (int st = 0; st < QS; ++st) asm volatile("" : "+v"(qf[st]));
+      qk_only(0);                           // scores of slice 0
+      step(no{}, yes{}, 0, HALF, 0);        // softmax 0, scores 1
+      // Tile u: wait for it (tile u + 1 may stay in flight), start loading
+      // tile u + 2 into the stage that held tile u - 2 (last read by the P.V
+      // steps of tile u - 1, which every wave has finished at the barrier),
+      // then steps 2u - 1 and 2u: scores from tile u, P.V from tile u - 1.
+      auto tile_body = [&](auto stage_c, int u) {
+        constexpr int S = decltype(stage_c)::value;
+        constexpr uint32_t kst = S * TB, vst = ((S + 3) % 4) * TB, nst = ((S + 2) % 4) * TB;
+        if (u + 1 < nkt)
+          wait_vmem<2 * DPW>();
+        else
+          wait_vmem<0>();
+        raw_barrier();
+        if (u + 2 < nkt) load_tile(u + 2, nst);
+        step_steady(2 * u - 1, kst, vst);
+        step_steady(2 * u, kst + HALF, vst + HALF);
+        if (u + 3 < nkt) load_ids(u + 3);
+      };
+      static_assert(Tl::STAGES == 4, "the tile loop is unrolled over four stages");
+      for (int u0 = 0; u0 < nkt; u0 += 4) {
+        if (u0 > 0) tile_body(std::integral_constant<int, 0>{}, u0);
+        if (u0 + 1 < nkt) tile_body(std::integral_constant<int, 1>{}, u0 + 1);
+        if (u0 + 2 < nkt) tile_body(std::integral_constant<int, 2>{}, u0 + 2);
+        if (u0 + 3 < nkt) tile_body(std::integral_constant<int, 3>{}, u0 + 3);
+      }
+      // Epilogue: the last two P.V steps read V of the last tile.
+      const uint32_t vst = static_cast<uint32_t>((nkt - 1) % 4) * TB;
+      step(yes{}, no{}, 2 * nkt - 1, 0, vst);
+      pv_only(vst + HALF);
     }
 
     if (wave_active) {
@@ -490,7 +709,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
         char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
         // lane holds O^T[d = 32 dt + 8 q + 4 hh + r][token col]
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int d = 32 * dt + 8 * q + 4 * hh;
@@ -501,6 +720,21 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
       }
     }
   }
+}
+
+// block_tables comes in again as a restrict pointer: nothing in the kernel
+// writes it, so its wave-uniform entries are read with scalar loads.
+template <int D, int HW>
+__global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
+  // No static LDS: the dynamic array starts at address 0, so fragment
+  // addresses are a per-lane offset plus an immediate.
+  extern __shared__ uint4 lds[];
+  int* item_sh = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + 2 * Bf16Tile<D>::STAGES * Bf16Tile<D>::TB);
+  // The load view is offset by an opaque zero so that the two views are
+  // distinct values (identical arguments would defeat the restrict hint).
+  uint32_t zero = 0;
+  asm volatile("" : "+s"(zero));
+  prefill_bf16_items<D, HW>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -634,11 +868,6 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
-constexpr size_t bf16_lds_bytes() {
-  return sizeof(uint4) * (2 * 2 * Bf16Tile<D>::CHUNKS + 1);
-}
-
 template <bool BF16, int D, int HW>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
@@ -657,7 +886,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   if (items_ub == 0) return hipSuccess;
   // Workgroups pull items from the queue until it is empty: enough of them
   // to fill every CU (bf16: one 8-wave workgroup per CU; fp32: four 4-wave).
-  const int64_t grid = std::min<int64_t>(items_ub, BF16 ? 512 : 1024);
+  const int64_t grid = std::min<int64_t>(items_ub, BF16 ? 256 : 1024);
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
@@ -681,7 +910,7 @@ hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
 
 template <int D, int HW>
 hipError_t allow_lds() {
-  // The double-buffered bf16 tiles take 64 KB of dynamic LDS at D = 128.
+  // The four bf16 K and V stages take 128 KB of dynamic LDS at D = 128.
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, HW>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bf16_lds_bytes<D>()));
 }
