@@ -194,16 +194,6 @@ __device__ inline int64_t next_item(const AttnArgs& a, int* item_sh) {
   return item;
 }
 
-// 16 bytes at byte offset off of a block's head slice. The block base is
-// wave-uniform, so the load goes through a buffer resource built in scalar
-// registers and the per-lane offset is the only vector operand; reads at or
-// past rec bytes return zero.
-__device__ inline uint4 load_row16(const char* base, uint32_t rec, uint32_t off) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, static_cast<int>(rec), kBufferFlags);
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
-
 // ---------------------------------------------------------------- bf16 ----
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -391,13 +381,24 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 #pragma unroll
       for (int st = 0; st < QS; ++st)
         qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * st));
+      // Pre-scaled by scale * log2(e), so the scores come out in log2 units.
+      // Rounding the scaled Q to bf16 perturbs each product term by at most
+      // 2^-9 relative, far below the bf16 rounding of the weights.
+#pragma unroll
+      for (int st = 0; st < QS; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[st][e] = static_cast<__bf16>(static_cast<float>(qf[st][e]) * c_scale);
     }
     f32x16 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float l_run = 0.f;
+    // Scores are kept relative to the running maximum m in log2 units: every
+    // score chain after the first starts from negm = -m (all 16 entries)
+    // instead of zero, so the weights are plain exp2 of the chain's result.
+    f32x16 negm;
 
     // Software pipeline over 32-key slices j: step j runs the softmax of
     // slice j, the score chain of slice j + 1 and P.V of slice j - 1, so the
@@ -417,13 +418,13 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       const uint2 lo2 = __builtin_bit_cast(uint2, lo), hi2 = __builtin_bit_cast(uint2, hi);
       return __builtin_bit_cast(bf16x8, make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
     };
-    // Weights against the running reference m_run; four partial sums keep
-    // the adds from forming one serial chain.
+    // Weights of a slice; four partial sums keep the adds from forming one
+    // serial chain.
     auto weights = [&](const float (&sc)[16], float (&w)[16]) {
       float part[4];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        w[i] = fast_exp2(__builtin_fmaf(sc[i], c_scale, -m_run));
+        w[i] = fast_exp2(sc[i]);
         part[i & 3] = i < 4 ? w[i] : part[i & 3] + w[i];
       }
       return (part[0] + part[1]) + (part[2] + part[3]);
@@ -436,25 +437,30 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[q2][e] = static_cast<__bf16>(w[8 * q2 + e]);
     };
-    // The reference stands while no weight of the slice exceeds 2^8 (checked
-    // through the lane's sum, which also catches inf and NaN). Otherwise the
-    // slice's true maximum is taken across the two lane halves of each token,
-    // the accumulators (which already hold P.V of the previous slice) are
-    // rescaled and the weights recomputed. The first slice always lands here
-    // (m_run starts at -inf).
-    auto settle = [&](const float (&sc)[16], float (&w)[16], float& lsum, bf16x8 (&p)[2]) {
+    // The reference m stands while no weight of the slice exceeds 2^8
+    // (checked through the lane's sum, which also catches inf and NaN).
+    // Otherwise the slice's maximum is taken across the two lane halves of
+    // each token; where it is above m, m moves up to it: the accumulators
+    // (which already hold P.V of the previous slice) and l are rescaled, and
+    // the slice's scores, negm and sn (the next slice's chain, started from
+    // the old m) are shifted. Then the weights are recomputed.
+    auto settle = [&](float (&sc)[16], float (&w)[16], float& lsum, bf16x8 (&p)[2], f32x16* sn) {
       if (__any(!(lsum <= kRescaleBound))) {
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * c_scale;
-        const float m_new = fmaxf(m_run, tmax);
-        if (m_new > m_run) {
-          const float alpha = fast_exp2(m_run - m_new);
+        const float delta = fmaxf(fmaxf(tmax, __shfl_xor(tmax, 32)), 0.f);
+        if (delta > 0.f) {
+          const float alpha = fast_exp2(-delta);
           l_run *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
-          m_run = m_new;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            negm[i] -= delta;
+            sc[i] -= delta;
+          }
+          if (sn != nullptr) *sn -= delta;
         }
         lsum = weights(sc, w);
         pack(w, p);
@@ -469,108 +475,39 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 #pragma unroll
       for (int i = 0; i < 16; ++i) s_cur[i] = 8 * (i >> 2) + (i & 3) <= t ? s_cur[i] : -INFINITY;
     };
-    // Step j: softmax of slice j, with P.V of slice j - 1 (PV) and the score
-    // chain of slice j + 1 (QK). Every wave runs every slice of the tile's
-    // keys; keys a lane must not see are masked, so slices past a wave's
-    // last token cost work but change nothing (their weights are zero and
-    // their V rows finite: real keys, or zeros past kend).
-    auto step = [&](auto pv_c, auto qk_c, int j, uint32_t ko, uint32_t vo) {
-      constexpr bool PV = decltype(pv_c)::value, QK = decltype(qk_c)::value;
+    // Step j: softmax of slice j with P.V of slice j - 1 and (QK) the score
+    // chain of slice j + 1. Every wave runs every slice of the tile's keys;
+    // keys a lane must not see are masked, so slices past a wave's last
+    // token cost work but change nothing (their weights are zero and their V
+    // rows finite: real keys, or zeros past kend).
+    //
+    // Scheduled by hand: the MFMAs go out one at a time, each followed by a
+    // share of the softmax's vector work (weights, their sum, the bf16
+    // packing), and fragment reads run ahead of their MFMAs. Scheduling
+    // fences hold that order; left alone, the compiler bunches the vector
+    // work ahead of the first MFMA.
+    auto step = [&](auto qk_c, int j, uint32_t ko, uint32_t vo) {
+      constexpr bool QK = decltype(qk_c)::value;
       if (32 * j + 31 > wave_first) mask_cur(j);
-      // Two phases, each reading half of the fragments (V rows of one
-      // 16-key group, half of the K k-steps) before its MFMAs.
-      bf16x8 va[2][DT], kf[QS];
-      float sc[16], w[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = s_cur[i];
-      if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) va[0][dt] = read_v(vo, 0, dt);
-      }
-      if constexpr (QK) {
-#pragma unroll
-        for (int st = 0; st < QS / 2; ++st) kf[st] = read_k(ko, st);
-      }
-      float lsum = weights(sc, w);
-      bf16x8 p[2];
-      pack(w, p);
-      if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][dt], p_prev[0], o[dt], 0, 0, 0);
-      }
-      f32x16 sn;
-      if constexpr (QK) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sn[i] = 0.f;
-#pragma unroll
-        for (int st = 0; st < QS / 2; ++st) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sn, 0, 0, 0);
-      }
-      if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) va[1][dt] = read_v(vo, 1, dt);
-      }
-      if constexpr (QK) {
-#pragma unroll
-        for (int st = QS / 2; st < QS; ++st) kf[st] = read_k(ko, st);
-      }
-      if constexpr (PV) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][dt], p_prev[1], o[dt], 0, 0, 0);
-      }
-      if constexpr (QK) {
-#pragma unroll
-        for (int st = QS / 2; st < QS; ++st) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sn, 0, 0, 0);
-      }
-      if constexpr (PV && QK) {
-        // Issue order: phase 1's reads, some weights while they land, its
-        // MFMAs one at a time with weight math between them; then phase 2.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT + QS / 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-#pragma unroll
-        for (int k = 0; k < DT + QS / 2; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT + QS / 2, 0);
-#pragma unroll
-        for (int k = 0; k < DT + QS / 2; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        }
-      }
-      settle(sc, w, lsum, p);
-      p_prev[0] = p[0];
-      p_prev[1] = p[1];
-      if constexpr (QK) s_cur = sn;
-    };
-    // The steady step, scheduled by hand: the MFMAs go out one at a time,
-    // each followed by a share of the softmax's vector work (weights, their
-    // sum, the bf16 packing), and each half of the fragment reads goes out
-    // ahead of the MFMAs that use it. Scheduling fences hold that order; left
-    // alone, the compiler bunches the vector work ahead of the first MFMA.
-    auto step_steady = [&](int j, uint32_t ko, uint32_t vo) {
-      if (32 * j + 31 > wave_first) mask_cur(j);
-      constexpr int M = 2 * DT + QS;  // MFMAs
-      // Vector work items. Item k < 20 runs three independent operations:
-      // the scaled score of element k, exp2 of element k - 2 and the partial
-      // sum of element k - 4, so that no operation waits on the one before
-      // it. Then the total (item 20) and the eight bf16 pairs (21 .. 28).
-      constexpr int NW = 20 + 1 + 8;
-      float sc[16], t[16], w[16], part[4], lsum = 0.f;
+      constexpr int M = 2 * DT + QS;  // MFMA slots (the score chain's only with QK)
+      // Vector work items. Item k < 18 runs two independent operations: exp2
+      // of element k and the partial sum of element k - 2. Then the total
+      // (item 18) and the eight bf16 pairs (19 .. 26).
+      constexpr int NW = 18 + 1 + 8;
+      float sc[16], w[16], part[4], lsum = 0.f;
       bf16x8 p[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc[i] = s_cur[i];
       auto work = [&](auto k_c) {
         constexpr int k = decltype(k_c)::value;
-        if constexpr (k < 20) {
-          if constexpr (k < 16) t[k] = __builtin_fmaf(sc[k], c_scale, -m_run);
-          if constexpr (k >= 2 && k < 18) w[k - 2] = fast_exp2(t[k - 2]);
-          if constexpr (k >= 4 && k < 8) part[k - 4] = w[k - 4];
-          if constexpr (k >= 8) part[(k - 4) & 3] += w[k - 4];
-        } else if constexpr (k == 20) {
+        if constexpr (k < 18) {
+          if constexpr (k < 16) w[k] = fast_exp2(sc[k]);
+          if constexpr (k >= 2 && k < 6) part[k - 2] = w[k - 2];
+          if constexpr (k >= 6) part[(k - 2) & 3] += w[k - 2];
+        } else if constexpr (k == 18) {
           lsum = (part[0] + part[1]) + (part[2] + part[3]);
         } else {
-          constexpr int e = k - 21;  // weights 2e, 2e + 1 -> P^T slots of p[e / 4]
+          constexpr int e = k - 19;  // weights 2e, 2e + 1 -> P^T slots of p[e / 4]
           p[e / 4][2 * (e % 4)] = static_cast<__bf16>(w[2 * e]);
           p[e / 4][2 * (e % 4) + 1] = static_cast<__bf16>(w[2 * e + 1]);
         }
@@ -588,7 +525,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       auto issue_read = [&](auto m_c) {
         constexpr int m = decltype(m_c)::value;
         if constexpr (m % 2 == 0) {
-          fr[m] = read_k(ko, m / 2);
+          if constexpr (QK) fr[m] = read_k(ko, m / 2);
         } else {
           constexpr int i = (m - 1) / 2;
           fr[m] = read_v(vo, i / DT, i % DT);
@@ -603,12 +540,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         constexpr int m = decltype(m_c)::value;
         if constexpr (m % 2 == 0) {
           constexpr int st = m / 2;
-          if constexpr (st == 0) {
-            const f32x16 zero = {};
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[0], zero, 0, 0, 0);
-          } else {
-            sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[st], sn, 0, 0, 0);
-          }
+          if constexpr (QK) sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], qf[st], st == 0 ? negm : sn, 0, 0, 0);
         } else {
           constexpr int i = (m - 1) / 2, q2 = i / DT, dt = i % DT;
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m], p_prev[q2], o[dt], 0, 0, 0);
@@ -618,13 +550,15 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         static_for<4 + (NW - 4) * m / M, 4 + (NW - 4) * (m + 1) / M>(work);
         fence();
       });
-      settle(sc, w, lsum, p);
+      settle(sc, w, lsum, p, QK ? &sn : nullptr);
       p_prev[0] = p[0];
       p_prev[1] = p[1];
-      s_cur = sn;
+      if constexpr (QK) s_cur = sn;
     };
-    // The score chain of slice 0 alone, and P.V of the last slice alone.
-    auto qk_only = [&](uint32_t ko) {
+    // The score chain of slice 0 from zero; then the first softmax, which
+    // sets m to the slice's maximum (finite: every lane sees key 0), and the
+    // chain of slice 1 from -m.
+    auto first_steps = [&](uint32_t ko) {
       bf16x8 kf[QS];
 #pragma unroll
       for (int st = 0; st < QS; ++st) kf[st] = read_k(ko, st);
@@ -632,7 +566,29 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       for (int i = 0; i < 16; ++i) s_cur[i] = 0.f;
 #pragma unroll
       for (int st = 0; st < QS; ++st) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s_cur, 0, 0, 0);
+      if (31 > wave_first) mask_cur(0);
+      float sc[16], w[16];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sc[i] = s_cur[i];
+        tmax = fmaxf(tmax, sc[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        negm[i] = -tmax;
+        sc[i] -= tmax;
+      }
+      l_run = weights(sc, w);
+      pack(w, p_prev);
+#pragma unroll
+      for (int st = 0; st < QS; ++st) kf[st] = read_k(ko + HALF, st);
+      s_cur = negm;
+#pragma unroll
+      for (int st = 0; st < QS; ++st) s_cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], s_cur, 0, 0, 0);
     };
+    // P.V of the last slice alone.
     auto pv_only = [&](uint32_t vo) {
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2) {
@@ -669,8 +625,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       // memory count, which would also wait for the tile loads in flight.
 #pragma unroll
       for (int st = 0; st < QS; ++st) asm volatile("" : "+v"(qf[st]));
-      qk_only(0);                           // scores of slice 0
-      step(no{}, yes{}, 0, HALF, 0);        // softmax 0, scores 1
+      first_steps(0);                       // scores of slices 0 and 1, softmax 0
       // Tile u: wait for it (tile u + 1 may stay in flight), start loading
       // tile u + 2 into the stage that held tile u - 2 (last read by the P.V
       // steps of tile u - 1, which every wave has finished at the barrier),
@@ -684,8 +639,8 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
           wait_vmem<0>();
         raw_barrier();
         if (u + 2 < nkt) load_tile(u + 2, nst);
-        step_steady(2 * u - 1, kst, vst);
-        step_steady(2 * u, kst + HALF, vst + HALF);
+        step(yes{}, 2 * u - 1, kst, vst);
+        step(yes{}, 2 * u, kst + HALF, vst + HALF);
         if (u + 3 < nkt) load_ids(u + 3);
       };
       static_assert(Tl::STAGES == 4, "the tile loop is unrolled over four stages");
@@ -697,7 +652,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       }
       // Epilogue: the last two P.V steps read V of the last tile.
       const uint32_t vst = static_cast<uint32_t>((nkt - 1) % 4) * TB;
-      step(yes{}, no{}, 2 * nkt - 1, 0, vst);
+      step(no{}, 2 * nkt - 1, 0, vst);
       pv_only(vst + HALF);
     }
 
