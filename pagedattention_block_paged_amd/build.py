@@ -20,6 +20,9 @@ def hipcc_command(out: str = LIB, extra=()) -> list:
         # MFMA accumulators in VGPRs: the softmax works on them with VALU
         # instructions, and AGPR accumulators cost a copy each way per tile
         "-mllvm", "-amdgpu-mfma-vgpr-form",
+        # every atomic here is issued by one lane; the wave-level atomic
+        # rewrite would read the result back at once and wait for it
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-Wall", "-Wno-unused-function",
         "-I", os.path.join(ROOT, "include"),
         *extra,

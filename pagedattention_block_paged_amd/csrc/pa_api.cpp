@@ -319,7 +319,7 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
   w.tile_start_off = 0;
   w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
   w.order_off = w.counter_off + 256;
-  w.ml_off = w.order_off + align(size_t(kMaxSortedTiles) * 2 * sizeof(int32_t));
+  w.ml_off = w.order_off + align(size_t(kMaxSortedTiles) * kTileRecord * sizeof(int32_t));
   // split-K partials, one set per (new token, query head, partition) of the
   // decode kernel's sequences
   w.o_off = w.ml_off + align(size_t(T) * Hq * parts * sizeof(float2));

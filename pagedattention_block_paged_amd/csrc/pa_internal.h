@@ -69,13 +69,16 @@ struct AttnArgs {
   float2* ws_ml;        // [S][Hq][max_parts] (running max in log2 units, sum of weights)
   // prefill work list
   int32_t* tile_start;    // [S + 1] exclusive prefix sum of prefill q-tiles per sequence
-  int32_t* tile_order;    // [kMaxSortedTiles][2] (sequence, tile) of the q-tiles by decreasing key count (if they fit)
+  int32_t* tile_order;    // [kMaxSortedTiles][kTileRecord] per rank of the q-tiles by decreasing key count (if
+                          // they fit): sequence, tile, query start, query count, cached context, length,
+                          // 2 unused, then the sequence's first 8 block-table entries
   int32_t* work_counter;  // prefill work-queue head, zeroed by the plan kernel
 };
 
 // Up to this many prefill q-tiles are sorted by cost (longest first) before
 // the prefill kernel takes them from a queue; beyond it they go in order.
 constexpr int kMaxSortedTiles = 4096;
+constexpr int kTileRecord = 16;  // int32 words per ranked-tile record
 
 struct WorkspaceLayout {
   size_t tile_start_off, counter_off, order_off, ml_off, o_off, total;

@@ -77,7 +77,8 @@ constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 // One block of 1024 threads: per-sequence tile counts, exclusive scan into
 // tile_start, cost-sorted tile order (if it fits), queue head reset.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const int32_t* ctx_lens,
-                                                    const int32_t* seq_lens, int64_t S, int64_t T, int64_t MB,
+                                                    const int32_t* seq_lens, const int32_t* block_tables,
+                                                    int64_t bt_row, int64_t S, int64_t T, int64_t MB,
                                                     int64_t G, int qtile, int32_t* tile_start, int32_t* tile_order,
                                                     int32_t* counter) {
   __shared__ int32_t part[1024];
@@ -148,18 +149,34 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
       __syncthreads();
     }
   }
-  // (sequence, local tile) by rank, so that workgroups need no search
+  // One record per rank: the tile, its sequence's clamped lengths and the
+  // block ids of its first key tiles, so that a workgroup can start an item's
+  // first K/V loads after a single load.
   for (int i = tid; i < total; i += 1024) {
     const int32_t t = static_cast<int32_t>(0xffffffffu - uint32_t(keys[i]));
     const int32_t sq = tile_seq[t];
-    tile_order[2 * i] = sq;
-    tile_order[2 * i + 1] = t - tile_start[sq];
+    const int64_t q0 = min(max(static_cast<int64_t>(qsl[sq]), int64_t(0)), T);
+    const int64_t n = min(max(static_cast<int64_t>(qsl[sq + 1]), q0), T) - q0;
+    const int64_t Lc = min(max(static_cast<int64_t>(seq_lens[sq]), int64_t(0)), MB * kBlockTokens);
+    const int64_t C = min(max(static_cast<int64_t>(ctx_lens[sq]), int64_t(0)), Lc);
+    int4* rec = reinterpret_cast<int4*>(tile_order + kTileRecord * i);
+    rec[0] = make_int4(sq, t - tile_start[sq], static_cast<int32_t>(q0), static_cast<int32_t>(n));
+    rec[1] = make_int4(static_cast<int32_t>(C), static_cast<int32_t>(Lc), 0, 0);
+    // the block ids of the first two key tiles (8 blocks), as the table has them
+    const int32_t* row = block_tables + sq * bt_row;
+    auto id = [&](int j) { return row[min(int64_t(j), MB - 1)]; };
+    rec[2] = make_int4(id(0), id(1), id(2), id(3));
+    rec[3] = make_int4(id(4), id(5), id(6), id(7));
   }
 }
 
-// Which sequence and local tile a queue item names.
+// Which sequence and local tile a queue item names, with the sequence's
+// clamped query start, query count, cached context and length.
 struct TileRef {
   int64_t s, lt, g, hg;
+  int64_t q0, n, C, Lc;
+  bool ranked;        // from a plan record, which also holds
+  int4 ids_lo, ids_hi;  // the sequence's table entries 0 .. 3 and 4 .. 7
 };
 
 __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int64_t total_tiles) {
@@ -168,9 +185,18 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
   const int64_t rest = item / a.Hkv;
   r.hg = rest % n_hg;
   const int64_t rank = rest / n_hg;
-  if (total_tiles <= kMaxSortedTiles) {  // the plan kernel listed (sequence, tile) by rank
-    r.s = a.tile_order[2 * rank];
-    r.lt = a.tile_order[2 * rank + 1];
+  if (total_tiles <= kMaxSortedTiles) {  // the plan kernel wrote one record per rank
+    const int4* rec = reinterpret_cast<const int4*>(a.tile_order + kTileRecord * rank);
+    const int4 r0 = rec[0], r1 = rec[1], r2 = rec[2], r3 = rec[3];
+    r.s = r0.x;
+    r.lt = r0.y;
+    r.q0 = r0.z;
+    r.n = r0.w;
+    r.C = r1.x;
+    r.Lc = r1.y;
+    r.ranked = true;
+    r.ids_lo = r2;
+    r.ids_hi = r3;
     return r;
   }
   const int64_t t = rank;
@@ -181,6 +207,12 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
   }
   r.s = lo;
   r.lt = t - a.tile_start[lo];
+  r.ranked = false;
+  r.ids_lo = r.ids_hi = make_int4(0, 0, 0, 0);
+  r.q0 = min(max(static_cast<int64_t>(a.qsl[lo]), int64_t(0)), a.T);
+  r.n = min(max(static_cast<int64_t>(a.qsl[lo + 1]), r.q0), a.T) - r.q0;
+  r.Lc = min(max(static_cast<int64_t>(a.seq_lens[lo]), int64_t(0)), a.MB * kBlockTokens);
+  r.C = min(max(static_cast<int64_t>(a.ctx_lens[lo]), int64_t(0)), r.Lc);
   return r;
 }
 
@@ -328,15 +360,26 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
   }
   auto blk_of = [&](int i) { return (64 * (wave + kPWaves * i) / CPR) / kBlockTokens; };
 
-  for (int64_t item = next_item(a, item_sh); item < n_items; item = next_item(a, item_sh)) {
+  // A workgroup's first item is its own index (items are ranked longest
+  // first, so this is the first round of a longest-first assignment); later
+  // items come from the queue. The next item is claimed while the current
+  // one's last key tile is in flight (thread 0 issues the atomic and keeps the
+  // result), so the claim's round trip overlaps compute; the queue order is
+  // still close to the order in which workgroups run out of work.
+  int64_t item = blockIdx.x;
+  while (item < n_items) {
     const TileRef tr = locate(a, item, n_hg, total_tiles);
     // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
     const int64_t s = tr.s, g = tr.g;
     const int lt = static_cast<int>(tr.lt), hg = static_cast<int>(tr.hg);
-    const int64_t q0 = min(max(static_cast<int64_t>(a.qsl[s]), int64_t(0)), a.T);
-    const int n = static_cast<int>(min(max(static_cast<int64_t>(a.qsl[s + 1]), q0), a.T) - q0);
-    const int Lc = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
-    const int C = min(max(a.ctx_lens[s], 0), Lc);
+    const int64_t q0 = tr.q0;
+    const int n = static_cast<int>(tr.n);
+    const int Lc = static_cast<int>(tr.Lc);
+    const int C = static_cast<int>(tr.C);
+    int claimed = 0;  // thread 0: the queue position of the next item
+    auto claim = [&] {
+      if (tid == 0) claimed = atomicAdd(a.work_counter, 1);
+    };
     const int64_t h = g * G + hg * HW + hw;
     const int i0 = lt * QTB + tw * kWaveTokens;  // first token of this wave
     const bool wave_active = i0 < n;
@@ -358,6 +401,19 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     auto load_ids = [&](int t) {
 #pragma unroll
       for (int i = 0; i < DPW; ++i) ids[i] = bt[min(t * (KT / kBlockTokens) + blk_of(i), last_blk)];
+    };
+    // Tiles 0 and 1 (blocks 0 .. 7) take their ids from the item's plan
+    // record when it has one (read together with the item, picked by register
+    // selects), not from the table: no round trip before the first loads.
+    auto first_ids = [&](int t) {
+      if (!tr.ranked) return load_ids(t);
+#pragma unroll
+      for (int i = 0; i < DPW; ++i) {
+        const int j = min(t * (KT / kBlockTokens) + blk_of(i), last_blk);
+        const int4 q = j < 4 ? tr.ids_lo : tr.ids_hi;
+        const int jj = j & 3;
+        ids[i] = jj == 0 ? q.x : jj == 1 ? q.y : jj == 2 ? q.z : q.w;
+      }
     };
     // Rows at or past kend (only in the last tile) read past the resource and
     // land as zeros; their block index is clamped to a block the tile needs.
@@ -381,14 +437,17 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 #pragma unroll
       for (int st = 0; st < QS; ++st)
         qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * st));
-      // Pre-scaled by scale * log2(e), so the scores come out in log2 units.
-      // Rounding the scaled Q to bf16 perturbs each product term by at most
-      // 2^-9 relative, far below the bf16 rounding of the weights.
+    }
+    // Pre-scaled by scale * log2(e) once the loads have landed (after the
+    // first tiles' loads are out), so the scores come out in log2 units.
+    // Rounding the scaled Q to bf16 perturbs each product term by at most
+    // 2^-9 relative, far below the bf16 rounding of the weights.
+    auto scale_q = [&] {
 #pragma unroll
       for (int st = 0; st < QS; ++st)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[st][e] = static_cast<__bf16>(static_cast<float>(qf[st][e]) * c_scale);
-    }
+    };
     f32x16 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -604,16 +663,18 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 
     if (nkt > 0) {
       // Prologue: tiles 0 and 1 in flight, wait for tile 0 (and the Q loads).
-      load_ids(0);
+      first_ids(0);
       load_tile(0, 0);
       if (nkt > 1) {
-        load_ids(1);
+        first_ids(1);
         load_tile(1, TB);
         wait_vmem<2 * DPW>();
       } else {
         wait_vmem<0>();
       }
       raw_barrier();
+      // Claim point for short items: after the last tile's loads went out.
+      if (nkt <= 2) claim();
       if (nkt > 2) {
         load_ids(2);
         load_tile(2, 2 * TB);
@@ -625,6 +686,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       // memory count, which would also wait for the tile loads in flight.
 #pragma unroll
       for (int st = 0; st < QS; ++st) asm volatile("" : "+v"(qf[st]));
+      scale_q();
       first_steps(0);                       // scores of slices 0 and 1, softmax 0
       // Tile u: wait for it (tile u + 1 may stay in flight), start loading
       // tile u + 2 into the stage that held tile u - 2 (last read by the P.V
@@ -633,12 +695,17 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       auto tile_body = [&](auto stage_c, int u) {
         constexpr int S = decltype(stage_c)::value;
         constexpr uint32_t kst = S * TB, vst = ((S + 3) % 4) * TB, nst = ((S + 2) % 4) * TB;
+        // Wave 0's claim (issued after the last tile's loads) may stay in
+        // flight through the last tile.
         if (u + 1 < nkt)
           wait_vmem<2 * DPW>();
+        else if (wave == 0)
+          wait_vmem<1>();
         else
           wait_vmem<0>();
         raw_barrier();
         if (u + 2 < nkt) load_tile(u + 2, nst);
+        if (u + 2 == nkt) claim();
         step(yes{}, 2 * u - 1, kst, vst);
         step(yes{}, 2 * u, kst + HALF, vst + HALF);
         if (u + 3 < nkt) load_ids(u + 3);
@@ -656,6 +723,10 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       pv_only(vst + HALF);
     }
 
+    if (nkt <= 0) claim();
+    // The claimed item goes to LDS before this item's output stores, so that
+    // waiting for the claim does not also wait for them.
+    if (tid == 0) *item_sh = static_cast<int>(gridDim.x) + claimed;  // queue items follow the first round
     if (wave_active) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int my_tok = i0 + col;
@@ -674,6 +745,11 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
           }
       }
     }
+    // Hand the claimed item to every wave. The barrier waits only for the
+    // LDS write, not for this item's output stores. Every wave reads the slot
+    // before its next barrier, and the slot is next written after one.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    item = __builtin_amdgcn_readfirstlane(*item_sh);
   }
 }
 
@@ -828,7 +904,8 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
   {
     ProfileScope ps(kPlan, stream);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.S, a.T, a.MB,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.block_tables,
+                       a.bt_row, a.S, a.T, a.MB,
                        a.Hq / a.Hkv, QTB, a.tile_start, a.tile_order, a.work_counter);
   }
   hipError_t e = hipGetLastError();
