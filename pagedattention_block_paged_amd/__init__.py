@@ -202,7 +202,10 @@ class profile:
 
     def __exit__(self, *exc):
         lib.pa_profile_stop()
-        for i, name in enumerate(KERNELS):
+        for i in range(len(KERNELS)):
+            name = lib.pa_profile_kernel_name(i).decode()
+            if not name:  # a library build with fewer kernels
+                break
             ms, n = ctypes.c_double(0), ctypes.c_int64(0)
             _check(lib.pa_profile_kernel(i, ctypes.byref(ms), ctypes.byref(n)))
             if n.value:

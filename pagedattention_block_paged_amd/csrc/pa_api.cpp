@@ -278,10 +278,78 @@ pa_status hip_status(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// A stream of the library's own and two events per (host thread, device),
+// for running the chunked prefill beside the decode kernel. Created on first
+// use and kept until the process ends (never destroyed: the runtime may be
+// gone by the time thread-local destructors run).
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool failed = false;
+};
+
+SideStream* side_stream_for(hipStream_t stream) {
+  constexpr int kMaxDevices = 64;
+  static thread_local SideStream side[kMaxDevices];
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = side[dev];
+  if (ss.failed) return nullptr;
+  if (!ss.stream) {
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess || (cur != dev && hipSetDevice(dev) != hipSuccess)) {
+      ss.failed = true;
+      return nullptr;
+    }
+    // default priority, no implicit synchronisation with the null stream
+    const bool ok = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking) == hipSuccess &&
+                    hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+                    hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (!ok) {
+      ss.failed = true;
+      return nullptr;
+    }
+  }
+  return &ss;
+}
+
+// K/V bytes the decode could read at most: every sequence at the table's full
+// width. Above this the decode kernel runs long enough that running the
+// prefill beside it pays for the cross-stream hand-off (a few microseconds).
+constexpr double kBesideMinDecodeBytes = 4e9;
+
+// Whether the prefill runs beside the decode: bf16, a decode that may be long,
+// and more query tokens than one per sequence by at least one prefill chunk
+// (a sequence on the prefill path has more than 16 / G new tokens), so that
+// batches of decodes alone do not pay for an idle second stream.
+bool prefill_beside_decode(const pa::AttnArgs& a) {
+  if (a.elem != pa::Elem::BF16) return false;
+  const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * 2.0;
+  const int64_t G = a.Hq / a.Hkv;
+  return kv_bound >= kBesideMinDecodeBytes && a.T - a.S >= pa::kMaxDecodeColumns / G + 1;
+}
+
+// The decode kernel (HBM-bound) and the chunked prefill (MFMA-bound) work on
+// disjoint rows of `out` and read only the inputs. For large mixed batches in
+// bf16 the prefill runs on a second stream, forked from and joined back into
+// `stream`, on a few CUs chosen by the plan kernel while the decode streams
+// on the rest; otherwise the two run one after the other on `stream`.
 pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream) {
   if (a.S == 0 || a.T == 0) return PA_OK;
+  SideStream* side = prefill_beside_decode(a) ? side_stream_for(stream) : nullptr;
+  if (!side) {
+    PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
+    PA_TRY(hip_status(pa::launch_prefill(a, stream, false), "prefill launch"));
+    return PA_OK;
+  }
+  PA_TRY(hip_status(hipEventRecord(side->fork, stream), "fork event"));
+  PA_TRY(hip_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork wait"));
+  // prefill first, so that its workgroups take their CUs before the decode's
+  PA_TRY(hip_status(pa::launch_prefill(a, side->stream, true), "prefill launch"));
   PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
-  PA_TRY(hip_status(pa::launch_prefill(a, stream), "prefill launch"));
+  PA_TRY(hip_status(hipEventRecord(side->join, side->stream), "join event"));
+  PA_TRY(hip_status(hipStreamWaitEvent(stream, side->join, 0), "join wait"));
   return PA_OK;
 }
 

@@ -72,7 +72,8 @@ struct AttnArgs {
   int32_t* tile_order;    // [kMaxSortedTiles][kTileRecord] per rank of the q-tiles by decreasing key count (if
                           // they fit): sequence, tile, query start, query count, cached context, length,
                           // 2 unused, then the sequence's first 8 block-table entries
-  int32_t* work_counter;  // prefill work-queue head, zeroed by the plan kernel
+  int32_t* work_counter;  // [0] prefill work-queue head, zeroed by the plan kernel; [1] prefill workgroups that
+                          // run beside the decode kernel (set by the plan kernel)
 };
 
 // Up to this many prefill q-tiles are sorted by cost (longest first) before
@@ -104,7 +105,11 @@ struct ProfileScope {
 };
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
+// Decode kernel, then the partition reduce (decode.hip).
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream);
+// Plan kernel, then the chunked-prefill kernel (prefill.hip). `beside`: the
+// prefill runs concurrently with the decode kernel (another stream), on the
+// share of the CUs the plan kernel sets (bf16 only).
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside);
 
 }  // namespace pa

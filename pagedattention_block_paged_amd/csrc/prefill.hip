@@ -74,14 +74,29 @@ constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 
+// Cost model for running the prefill beside the decode kernel (measured on
+// MI355X at head size 128): a prefill workgroup computes about 4.7 TFLOP/s
+// and spends about 6 us per item outside its key loop; the decode reads
+// about 6.6 TB/s over all 256 CUs.
+constexpr float kPrefillFlopPerCuUs = 4.7e6f;
+constexpr float kPrefillItemCuUs = 6.0f;
+constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
+
 // One block of 1024 threads: per-sequence tile counts, exclusive scan into
-// tile_start, cost-sorted tile order (if it fits), queue head reset.
+// tile_start, cost-sorted tile order (if it fits), queue head reset, and the
+// number of prefill workgroups to run when the prefill shares the GPU with
+// the decode kernel: enough CUs that the prefill work takes about half as
+// long as the decode work on the rest (all slots when there is no decode
+// work).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const int32_t* ctx_lens,
                                                     const int32_t* seq_lens, const int32_t* block_tables,
                                                     int64_t bt_row, int64_t S, int64_t T, int64_t MB,
-                                                    int64_t G, int qtile, int32_t* tile_start, int32_t* tile_order,
+                                                    int64_t G, int qtile, int64_t Hq, int64_t D,
+                                                    int64_t kv_token_bytes, int items_per_tile, int slots,
+                                                    int beside, int32_t* tile_start, int32_t* tile_order,
                                                     int32_t* counter) {
   __shared__ int32_t part[1024];
+  __shared__ float red_dec[1024], red_pre[1024];
   __shared__ uint64_t keys[kMaxSortedTiles];
   __shared__ int32_t tile_seq[kMaxSortedTiles];  // sequence of each tile (sorted case)
   const int tid = threadIdx.x;
@@ -97,9 +112,35 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
     return n >= 1 && !decode_path(n, G) ? static_cast<int32_t>((n + qtile - 1) / qtile) : 0;
   };
   int32_t sum = 0;
-  for (int64_t s = s0; s < s1; ++s) sum += tiles(qlen(s));
+  float dec_tokens = 0.f, pre_token_keys = 0.f;  // decode keys; prefill (query token, key) pairs (upper bound)
+  for (int64_t s = s0; s < s1; ++s) {
+    const int64_t n = qlen(s);
+    const int32_t nt = tiles(n);
+    sum += nt;
+    if (!beside || n < 1) continue;
+    const int64_t Lc = min(max(static_cast<int64_t>(seq_lens[s]), int64_t(0)), MB * kBlockTokens);
+    if (nt == 0) {
+      dec_tokens += static_cast<float>(Lc);
+    } else {
+      const int64_t C = min(max(static_cast<int64_t>(ctx_lens[s]), int64_t(0)), Lc);
+      for (int64_t i0 = 0; i0 < n; i0 += qtile)
+        pre_token_keys += static_cast<float>(min(int64_t(qtile), n - i0)) *
+                          static_cast<float>(min(C + min(n, i0 + qtile), Lc));
+    }
+  }
   part[tid] = sum;
+  red_dec[tid] = dec_tokens;
+  red_pre[tid] = pre_token_keys;
   __syncthreads();
+  if (beside) {
+    for (int off = 512; off > 0; off >>= 1) {
+      if (tid < off) {
+        red_dec[tid] += red_dec[tid + off];
+        red_pre[tid] += red_pre[tid + off];
+      }
+      __syncthreads();
+    }
+  }
   for (int off = 1; off < 1024; off <<= 1) {
     const int32_t v = tid >= off ? part[tid - off] : 0;
     __syncthreads();
@@ -129,7 +170,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
     run += nt;
   }
   if (tid == 1023) tile_start[S] = total;
-  if (tid == 0) *counter = 0;
+  if (tid == 0) {
+    counter[0] = 0;
+    const float pre = red_pre[0] * 4.f * static_cast<float>(D * Hq) / kPrefillFlopPerCuUs +
+                      static_cast<float>(total) * items_per_tile * kPrefillItemCuUs;
+    const float dec = red_dec[0] * static_cast<float>(kv_token_bytes) / kDecodeBytePerCuUs;
+    int active = 0;
+    if (total > 0)
+      active = (beside && dec > 0.f) ? static_cast<int>(ceilf(2.f * 256.f * pre / (pre + dec))) : slots;
+    counter[1] = min(max(active, total > 0 ? 1 : 0), slots);
+  }
   if (total > kMaxSortedTiles) return;  // uniform: tiles go in sequence order
   __syncthreads();
   // bitonic sort, descending (empty slots hold key 0 and sort last)
@@ -300,7 +350,8 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
                                                                         const int32_t* __restrict__ bt_all,
                                                                         lds_char* __restrict__ dma,
                                                                         const lds_char* __restrict__ rd,
-                                                                        int* item_sh) {
+                                                                        int* item_sh, int first_item,
+                                                                        int queue_base) {
   using Tl = Bf16Tile<D>;
   constexpr int KT = Tl::KT, CPR = Tl::CPR, DPW = Tl::DPW;
   constexpr uint32_t TB = Tl::TB, HALF = Tl::HALF, V0 = Tl::V0;
@@ -366,7 +417,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
   // one's last key tile is in flight (thread 0 issues the atomic and keeps the
   // result), so the claim's round trip overlaps compute; the queue order is
   // still close to the order in which workgroups run out of work.
-  int64_t item = blockIdx.x;
+  int64_t item = first_item;
   while (item < n_items) {
     const TileRef tr = locate(a, item, n_hg, total_tiles);
     // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
@@ -726,7 +777,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     if (nkt <= 0) claim();
     // The claimed item goes to LDS before this item's output stores, so that
     // waiting for the claim does not also wait for them.
-    if (tid == 0) *item_sh = static_cast<int>(gridDim.x) + claimed;  // queue items follow the first round
+    if (tid == 0) *item_sh = queue_base + claimed;  // queue items follow the first round
     if (wave_active) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int my_tok = i0 + col;
@@ -754,9 +805,15 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 }
 
 // block_tables comes in again as a restrict pointer: nothing in the kernel
-// writes it, so its wave-uniform entries are read with scalar loads.
+// writes it, so its wave-uniform entries are read with scalar loads. When the
+// prefill runs beside the decode kernel (`beside`), only the first
+// counter[1] workgroups (the plan kernel's share of the CUs) take items; the
+// others exit at once and leave their CUs to the decode.
 template <int D, int HW>
-__global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all) {
+__global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
+                                                                 int beside) {
+  const int active = beside ? min(a.work_counter[1], static_cast<int>(gridDim.x)) : static_cast<int>(gridDim.x);
+  if (static_cast<int>(blockIdx.x) >= active) return;
   // No static LDS: the dynamic array starts at address 0, so fragment
   // addresses are a per-lane offset plus an immediate.
   extern __shared__ uint4 lds[];
@@ -765,7 +822,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   // distinct values (identical arguments would defeat the restrict hint).
   uint32_t zero = 0;
   asm volatile("" : "+s"(zero));
-  prefill_bf16_items<D, HW>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh);
+  prefill_bf16_items<D, HW>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh, blockIdx.x, active);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -899,31 +956,40 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
   }
 }
 
+// Prefill workgroups to launch: enough to fill every CU (bf16: one 8-wave
+// workgroup per CU; fp32: four 4-wave), at most an upper bound on the items
+// that needs no lengths (every prefill sequence has more than 16 / G tokens).
 template <bool BF16, int D, int HW>
-hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
+int64_t prefill_slots(const AttnArgs& a) {
   constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
-  {
-    ProfileScope ps(kPlan, stream);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.block_tables,
-                       a.bt_row, a.S, a.T, a.MB,
-                       a.Hq / a.Hkv, QTB, a.tile_start, a.tile_order, a.work_counter);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // Upper bound on work without reading lengths: every prefill sequence has
-  // more than 16 / G tokens.
   const int64_t G = a.Hq / a.Hkv;
   const int64_t tiles_ub = a.T / QTB + std::min<int64_t>(a.S, a.T / (kMaxDecodeColumns / G + 1));
   const int64_t items_ub = tiles_ub * a.Hkv * (G / HW);
-  if (items_ub == 0) return hipSuccess;
-  // Workgroups pull items from the queue until it is empty: enough of them
-  // to fill every CU (bf16: one 8-wave workgroup per CU; fp32: four 4-wave).
-  const int64_t grid = std::min<int64_t>(items_ub, BF16 ? 256 : 1024);
+  return std::min<int64_t>(items_ub, BF16 ? 256 : 1024);
+}
+
+template <bool BF16, int D, int HW>
+hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, int64_t slots, bool beside) {
+  constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
+  ProfileScope ps(kPlan, stream);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.block_tables,
+                     a.bt_row, a.S, a.T, a.MB, a.Hq / a.Hkv, QTB, a.Hq, a.D, 2 * a.Hkv * a.D * (BF16 ? 2 : 4),
+                     static_cast<int>(a.Hkv * (a.Hq / a.Hkv / HW)), static_cast<int>(slots), beside ? 1 : 0,
+                     a.tile_start, a.tile_order, a.work_counter);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D, int HW>
+hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
+  const int64_t grid = prefill_slots<BF16, D, HW>(a);
+  hipError_t e = launch_plan<BF16, D, HW>(a, stream, grid, beside);
+  if (e != hipSuccess || grid == 0) return e;
+  // Workgroups pull items from the queue until it is empty.
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
       hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
-                         bf16_lds_bytes<D>(), stream, a, a.block_tables);
+                         bf16_lds_bytes<D>(), stream, a, a.block_tables, beside ? 1 : 0);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
                          a);
@@ -933,11 +999,11 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
 }
 
 template <bool BF16, int D>
-hipError_t launch_heads(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_heads(const AttnArgs& a, hipStream_t stream, bool beside) {
   const int64_t G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_typed<BF16, D, 4>(a, stream);
-  if (G % 2 == 0) return launch_typed<BF16, D, 2>(a, stream);
-  return launch_typed<BF16, D, 1>(a, stream);
+  if (G % 4 == 0) return launch_typed<BF16, D, 4>(a, stream, beside);
+  if (G % 2 == 0) return launch_typed<BF16, D, 2>(a, stream, beside);
+  return launch_typed<BF16, D, 1>(a, stream, beside);
 }
 
 template <int D, int HW>
@@ -949,7 +1015,7 @@ hipError_t allow_lds() {
 
 }  // namespace
 
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
   static const hipError_t lds_ok = [] {
     hipError_t e = hipSuccess;
     for (hipError_t r : {allow_lds<64, 1>(), allow_lds<64, 2>(), allow_lds<64, 4>(), allow_lds<128, 1>(),
@@ -959,8 +1025,8 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream) {
   }();
   if (lds_ok != hipSuccess) return lds_ok;
   const bool bf16 = a.elem == Elem::BF16;
-  if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream) : launch_heads<false, 64>(a, stream);
-  return bf16 ? launch_heads<true, 128>(a, stream) : launch_heads<false, 128>(a, stream);
+  if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, beside) : launch_heads<false, 64>(a, stream, beside);
+  return bf16 ? launch_heads<true, 128>(a, stream, beside) : launch_heads<false, 128>(a, stream, beside);
 }
 
 }  // namespace pa

@@ -1,5 +1,7 @@
 """A whole step (KV write, decode, split-K reduce, prefill planning and
-prefill) captured once in a HIP graph and replayed.
+prefill) captured once in a HIP graph and replayed, also when the library
+runs the prefill on a second stream forked from and joined back into the
+captured one.
 
 The library makes no allocation, synchronisation or memset on the launch
 stream, so `pa_step` can be captured as is. Each replay must equal the eager
@@ -37,10 +39,15 @@ def cases():
         ("mixed", W.build_workload("graph_mix", "bf16", 32, 8, 128, [300, 17, 0, 900, 45], [1, 1, 96, 1, 40],
                                    seed=4242)),
         ("f32 mixed", W.build_workload("graph_f32", "f32", 12, 4, 128, [200, 0, 33], [1, 70, 1], seed=4343)),
+        # a block table wide enough that the prefill runs on the library's own
+        # stream beside the decode: the fork and join are captured too
+        ("mixed, prefill beside decode", W.build_workload("graph_beside", "bf16", 32, 8, 128,
+                                                          [300, 17, 0, 900, 45, 2000], [1, 1, 96, 1, 40, 1],
+                                                          seed=4444, max_blocks=16384)),
     ]
 
 
-@pytest.mark.parametrize("idx", range(3))
+@pytest.mark.parametrize("idx", range(4))
 def test_graph_replay_equals_eager(pa, idx):
     name, wl = cases()[idx]
     say(f"[graph] {name}: S={wl.num_seqs} T={wl.num_tokens} {wl.dtype} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads}")

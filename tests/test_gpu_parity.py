@@ -140,6 +140,46 @@ def test_random_mixes(pa, idx):
     say(f"[mix {idx}] {e}")
 
 
+def beside_cases():
+    """Small bf16 batches with block tables wide enough (S x MB x 16 keys of K/V
+    above 4 GB) that the library runs the chunked prefill on its own stream
+    beside the decode kernel: mixes for each head grouping, a batch with no
+    decode and one with no prefill."""
+    rs = np.random.default_rng(4321)
+    cases = []
+    for i, (Hq, Hkv) in enumerate([(32, 8), (16, 8), (8, 8), (64, 8)]):
+        ctx = [int(x) for x in rs.integers(0, 3000, size=6)]
+        ql = [1, 1, int(rs.integers(40, 300)), 1, int(rs.integers(2, 90)), 1]
+        cases.append(W.build_workload(f"beside{i}", "bf16", Hq, Hkv, 128, ctx, ql, seed=900 + i, max_blocks=16384))
+    cases.append(W.build_workload("beside_prefill_only", "bf16", 32, 8, 128, [0, 700, 1500, 64], [300, 77, 129, 40],
+                                  seed=910, max_blocks=16384))
+    # decodes and short queries that stay on the decode kernel's path,
+    # with tokens enough for the library to take the two-stream path
+    cases.append(W.build_workload("beside_decode_only", "bf16", 32, 8, 128, [5, 2500, 900, 0], [1, 4, 4, 4],
+                                  seed=911, max_blocks=16384))
+    return cases
+
+
+@pytest.mark.parametrize("idx", range(6))
+def test_prefill_beside_decode(pa, idx):
+    wl = beside_cases()[idx]
+    bound = wl.num_seqs * wl.max_blocks * 16 * 2 * wl.num_kv_heads * wl.head_size * 2
+    G = wl.num_q_heads // wl.num_kv_heads
+    assert bound >= 4e9 and wl.num_tokens - wl.num_seqs >= 16 // G + 1, "the case must take the two-stream path"
+    say(f"[beside {idx}] Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} ctx={wl.context_lens.tolist()} "
+        f"q={wl.query_lens.tolist()} MB={wl.max_blocks}")
+    c = device_case(wl)
+    out = run_step(pa, wl, c)
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_workload(wl)
+    e = assert_within(to_f64(out), ref, wl.dtype, f"beside {idx}")
+    # the same batch again: deterministic, also across the two streams
+    out2 = run_step(pa, wl, c)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    say(f"[beside {idx}] {e}")
+
+
 def test_chunked_prefill_matches_whole_prefill(pa):
     """18 tokens as chunks of 8 + 8 + 2 through one pool equal one 18-token prefill."""
     whole = W.build_workload("whole", "bf16", 8, 2, 128, [0], [18], seed=77, num_blocks=8)
