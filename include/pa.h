@@ -30,6 +30,13 @@
  *  - Ordering: calls are asynchronous on `stream` (a hipStream_t; NULL is the
  *    default stream). pa_step orders the KV write before attention on that
  *    stream. No call synchronises the device or copies device data to the host.
+ *    For large bf16 batches that mix decodes and prefill chunks, pa_attention
+ *    and pa_step run the chunked prefill on a stream of the library's own
+ *    (one per host thread and device, created on first use, kept for the
+ *    life of the process, default priority), forked from `stream` and joined
+ *    back into it with events: the call's work still starts after, and ends
+ *    before, whatever is queued around it on `stream`, and it can be captured
+ *    in a HIP graph from `stream`.
  *  - Errors: host-side checks of the descriptors (null pointers, element
  *    types, ranks, extents, strides, alignment, supported sizes, workspace
  *    size) return a pa_status before anything is launched; the text of the
