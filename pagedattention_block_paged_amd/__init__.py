@@ -60,6 +60,12 @@ class Tensor(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    # One HIP runtime per process. torch ships its own libamdhip64; once it is
+    # loaded, libpa.so's dependency resolves to it. Loaded first, libpa.so
+    # would pull in the system runtime, torch would then load its own beside
+    # it, and the library's launches would find no device.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(Tensor)
     vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64

@@ -31,6 +31,19 @@ def test_exports_match_header(header, expected):
         assert hasattr(lib, name), name  # resolves the symbol in libpa.so
 
 
+def test_one_hip_runtime_per_process():
+    """Importing the binding first must not load a second HIP runtime beside
+    torch's: the library's launches would then find no device."""
+    import subprocess
+    import sys
+
+    code = ("import pagedattention_block_paged_amd, torch\n"
+            "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(maps))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "1", out.stdout + out.stderr
+
+
 def desc(shape, dtype, strides=None, data=FAKE):
     d = Tensor()
     d.data = data
