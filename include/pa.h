@@ -64,7 +64,9 @@ typedef enum {
   PA_ERR_STRIDE = 4,      /* layout not supported (inner dim not contiguous, misaligned) */
   PA_ERR_UNSUPPORTED = 5, /* block size != 16, head_size not 64/128, head ratio > 16 */
   PA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than pa_attention_workspace_size() */
-  PA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed */
+  PA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
+  PA_ERR_NO_BLOCKS = 8,   /* KV manager: too few free blocks; nothing changed */
+  PA_ERR_REQUEST = 9      /* KV manager: unknown or duplicate request id, or a token count it does not hold */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I32 = 2, PA_I64 = 3 } pa_dtype;

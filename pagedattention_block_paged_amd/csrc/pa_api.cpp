@@ -31,6 +31,26 @@ pa_status ok() {
   return PA_OK;
 }
 
+}  // namespace
+
+namespace pa {
+
+pa_status report(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status report_ok() { return ok(); }
+
+}  // namespace pa
+
+namespace {
+
 int64_t elem_bytes(int32_t dtype) {
   switch (dtype) {
     case PA_F32: return 4;
@@ -459,6 +479,8 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported size";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
+    case PA_ERR_REQUEST: return "unknown request or token count";
   }
   return "unknown status";
 }

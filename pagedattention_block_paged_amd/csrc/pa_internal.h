@@ -7,7 +7,14 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "pa.h"
+
 namespace pa {
+
+// Set the calling thread's pa_last_error() text and return `st`; report_ok()
+// clears it and returns PA_OK.
+pa_status report(pa_status st, const char* fmt, ...);
+pa_status report_ok();
 
 constexpr int kBlockTokens = 16;  // token slots per KV block
 constexpr int kWaves = 4;         // waves per workgroup (KV write, reduce, prefill)

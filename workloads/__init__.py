@@ -26,6 +26,7 @@ after the KV write the pool holds exactly ``seq_kv(s)`` at every position.
 from __future__ import annotations
 
 import dataclasses
+import hashlib
 import math
 from typing import Optional, Sequence
 
@@ -532,3 +533,29 @@ def fill_canary(t, dtype: str):
     else:
         t.view(torch.int16).fill_(_rng.CANARY_BF16_BITS)
     return t
+
+
+# ---------------------------------------------------------------------------
+# Token-stream inputs for multi-step runs (a request's tokens arrive and are
+# computed over several steps). A position's rows depend on every token id
+# up to and including it, as a model's K/V do, so requests that share a
+# token prefix share those rows exactly, which is what lets one request's
+# cached blocks serve another.
+
+
+def prefix_idents(tokens) -> np.ndarray:
+    """Identity of each position of a token sequence: a 62-bit chained digest
+    (BLAKE2b) of the token ids up to and including it."""
+    out = np.empty(len(tokens), np.int64)
+    prev = b"\0" * 8
+    for i, t in enumerate(tokens):
+        prev = hashlib.blake2b(prev + int(t).to_bytes(4, "little", signed=True), digest_size=8).digest()
+        out[i] = int.from_bytes(prev, "little") >> 2
+    return out
+
+
+def token_rows(seed: int, stream: int, idents, positions, heads: int, head_size: int, dtype: str) -> np.ndarray:
+    """Rows [n, heads, head_size] (host element type) addressed by (identity, position)."""
+    key = _rng.stream_key(seed, stream)
+    rows = _rows_np(key, np.asarray(idents, np.int64), np.asarray(positions, np.int64), heads * head_size, dtype)
+    return rows.reshape(-1, heads, head_size)
