@@ -351,6 +351,63 @@ def cpu_baseline(cfg: int, budget_s: float) -> dict:
     return out
 
 
+def host_manager(cfg: int, rounds: int = 6) -> dict:
+    """The library's host-side KV block manager producing the step inputs of a
+    workload: every sequence admitted (random token ids, prefix caching on)
+    with its cached context computed beforehand (untimed); then, timed, the
+    headline step itself (allocate_slots for every sequence's new tokens,
+    build_step, commit) and decode steps after it (one sampled token appended
+    per sequence). The allocate and commit loops are driven from Python, one
+    ctypes call per sequence, so they include that call overhead."""
+    import numpy as np
+
+    import workloads as W
+    from pagedattention_block_paged_amd.kv_manager import KVCacheManager
+
+    wl = W.config_workload(cfg)
+    S = wl.num_seqs
+    n = wl.query_lens.astype(np.int64)
+    C = wl.context_lens.astype(np.int64)
+    rs = np.random.default_rng(0)
+    t0 = time.perf_counter()
+    m = KVCacheManager(int(wl.num_blocks), 16, True)
+    for s in range(S):
+        m.add_request(s, rs.integers(0, 32000, int(C[s] + n[s]), dtype=np.int32))
+        if C[s]:
+            assert m.allocate_slots(s, int(C[s]))
+            m.commit(s, int(C[s]))
+    setup_s = time.perf_counter() - t0
+    ids = np.arange(S, dtype=np.int64)
+    width = wl.max_blocks + 1
+    out, rows = None, []
+    for r in range(rounds):
+        nn = n if r == 0 else np.ones(S, np.int64)
+        if r > 0:
+            for s in range(S):
+                m.append_tokens(s, [int(rs.integers(0, 32000))])
+        t1 = time.perf_counter()
+        for s in range(S):
+            assert m.allocate_slots(s, int(nn[s]))
+        t2 = time.perf_counter()
+        out = m.build_step(ids, nn, width, out=out)
+        t3 = time.perf_counter()
+        for s in range(S):
+            m.commit(s, int(nn[s]))
+        t4 = time.perf_counter()
+        rows.append(((t2 - t1) * 1e3, (t3 - t2) * 1e3, (t4 - t3) * 1e3))
+    dec = np.array(rows[1:])
+    return {
+        "workload": wl.name,
+        "requests": S,
+        "blocks_held": int(wl.num_blocks) - m.num_free_blocks,
+        "setup_s": setup_s,
+        "headline_step_ms": {"allocate_slots": rows[0][0], "build_step": rows[0][1], "commit": rows[0][2]},
+        "decode_step_ms_median": {k: float(np.median(dec[:, i]))
+                                  for i, k in enumerate(("allocate_slots", "build_step", "commit"))},
+        "note": "host CPU time; allocate_slots and commit loops include one ctypes call per request",
+    }
+
+
 def kernel_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed counter runs, if the kernel source is unchanged."""
     import hashlib
@@ -377,6 +434,8 @@ def main():
     ap.add_argument("--secondary", default="2,4,5,6", help="other workloads to measure, or 'none'")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-host-manager", action="store_true",
+                    help="skip timing the host KV block manager on the headline batch")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read",
                     help="cache eviction between timed steps (outside the step events)")
@@ -411,6 +470,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 x 1 GiB device-to-device copies")
+    mgr = None
+    if not args.no_host_manager:
+        mgr = host_manager(args.config)
+        log(f"[bench] host KV manager: {json.dumps(mgr)}")
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args.config, args.cpu_seconds)
@@ -470,6 +533,7 @@ def main():
             if head.get("prefill_alone") else "in the step",
         },
         "cpu_baseline": cpu,
+        "host_kv_manager": mgr,
         "kernels": head["kernels"],
         "secondary": secondary,
     }

@@ -152,6 +152,8 @@ pa_status pa_kv_manager_add_request(pa_kv_manager* m, int64_t req_id, const int3
   if (!prompt) return pa::report(PA_ERR_NULL, "pa_kv_manager_add_request: prompt is NULL");
   if (m->reqs.count(req_id)) return bad_request(req_id, "id already in use");
   Request r;
+  // room for generated tokens, so the first ones do not copy the prompt
+  r.tokens.reserve(static_cast<size_t>(n_prompt) + 256);
   r.tokens.assign(prompt, prompt + n_prompt);
   r.salt = salt;
   if (m->caching) {

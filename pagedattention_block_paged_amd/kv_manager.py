@@ -97,19 +97,19 @@ class KVCacheManager:
     def free(self, req_id: int):
         _check(lib.pa_kv_manager_free(self._h, req_id))
 
-    def build_step(self, req_ids: Sequence[int], num_new: Sequence[int], max_blocks: int) -> Dict[str, np.ndarray]:
+    def build_step(self, req_ids: Sequence[int], num_new: Sequence[int], max_blocks: int,
+                   out: Dict[str, np.ndarray] = None) -> Dict[str, np.ndarray]:
         """Host arrays of one pa_step: query_start_loc, seq_lens, context_lens,
-        block_tables, slot_mapping."""
+        block_tables, slot_mapping. ``out`` (a previous result of the same
+        shapes) is written in place, which saves re-faulting fresh pages."""
         ids = np.ascontiguousarray(req_ids, dtype=np.int64)
         nn = np.ascontiguousarray(num_new, dtype=np.int64)
         S = ids.size
-        out = {
-            "query_start_loc": np.zeros(S + 1, np.int32),
-            "seq_lens": np.zeros(S, np.int32),
-            "context_lens": np.zeros(S, np.int32),
-            "block_tables": np.zeros((S, max_blocks), np.int32),
-            "slot_mapping": np.zeros(int(nn.sum()) if S else 0, np.int64),
-        }
+        T = int(nn.sum()) if S else 0
+        shapes = {"query_start_loc": (S + 1,), "seq_lens": (S,), "context_lens": (S,),
+                  "block_tables": (S, max_blocks), "slot_mapping": (T,)}
+        if out is None or any(out[k].shape != v for k, v in shapes.items()):
+            out = {k: np.empty(v, np.int64 if k == "slot_mapping" else np.int32) for k, v in shapes.items()}
         _check(lib.pa_kv_manager_build_step(self._h, S, _ptr(ids), _ptr(nn), max_blocks,
                                             _ptr(out["query_start_loc"]), _ptr(out["seq_lens"]),
                                             _ptr(out["context_lens"]), _ptr(out["block_tables"]),
