@@ -69,7 +69,10 @@ typedef enum {
   PA_ERR_REQUEST = 9      /* KV manager: unknown or duplicate request id, or a token count it does not hold */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I32 = 2, PA_I64 = 3 } pa_dtype;
+/* PA_FP8_E4M3: OCP FP8 E4M3 codes (1 byte: sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits; no infinities; 0x7F / 0xFF are NaN; largest finite
+ * magnitude 448). Only for key_cache / value_cache, through the _fp8 calls. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I32 = 2, PA_I64 = 3, PA_FP8_E4M3 = 4 } pa_dtype;
 
 #define PA_MAX_DIMS 4
 
@@ -145,6 +148,42 @@ pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, 
                   const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
                   const pa_tensor* context_lens, float scale, void* workspace, size_t workspace_bytes,
                   pa_stream stream);
+
+/*
+ * 8-bit KV pool. The pages name 8-bit quantization of the KV cache, which
+ * halves the bytes every decode step reads, without fixing a format
+ * ("Serving models at scale with vLLM", section on quantization): here the
+ * pool holds PA_FP8_E4M3 codes with one fp32 scale for all keys and one for
+ * all values.
+ *  - pa_reshape_and_cache_fp8 stores code = nearest(x / k_scale) for each
+ *    element x of k (v / v_scale for v): the quotient is an IEEE fp32
+ *    division; nearest rounds to the closest code, ties to the even code,
+ *    magnitudes above 448 to +-448 (the sign kept), NaN to 0x7F. Negative
+ *    or past-the-pool slots are skipped as in pa_reshape_and_cache.
+ *  - pa_attention_fp8 / pa_step_fp8 read a key element back as
+ *    value(code) * k_scale and a value element as value(code) * v_scale
+ *    (exact), and otherwise compute what pa_attention / pa_step compute.
+ *   k, v, q, out   bf16 (q, out) and bf16 or f32 (k, v)
+ *   key_cache,     [NB, 16, Hkv, D] PA_FP8_E4M3, rows 16-byte aligned
+ *   value_cache
+ *   k_scale,       finite and > 0
+ *   v_scale
+ * Other arguments, errors and ordering as for the calls above; the f32/bf16
+ * calls reject an fp8 cache with PA_ERR_DTYPE.
+ */
+pa_status pa_reshape_and_cache_fp8(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
+                                   const pa_tensor* value_cache, const pa_tensor* slot_mapping, float k_scale,
+                                   float v_scale, pa_stream stream);
+pa_status pa_attention_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
+                           const pa_tensor* value_cache, const pa_tensor* block_tables,
+                           const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                           const pa_tensor* context_lens, float scale, float k_scale, float v_scale,
+                           void* workspace, size_t workspace_bytes, pa_stream stream);
+pa_status pa_step_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                      const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                      const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                      const pa_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
+                      size_t workspace_bytes, pa_stream stream);
 
 /*
  * Bytes of workspace pa_attention / pa_step need for these extents (the

@@ -121,8 +121,13 @@ def run_workload(wl, pool: Optional[np.ndarray] = None, num_threads: int = 0):
     if pool is None:
         pool = workloads.pool_host(wl)
     k, v = workloads.new_kv_host(wl)
-    reshape_and_cache(k, v, pool, wl.slot_mapping, wl.dtype)
     q = workloads.q_host(wl)
+    if wl.kv_dtype == "fp8":
+        reshape_and_cache_fp8(k, v, pool, wl.slot_mapping, wl.dtype, wl.k_scale, wl.v_scale)
+        out = attention_fp8(q, pool, wl.block_tables, wl.query_start_loc, wl.seq_lens, wl.context_lens, wl.scale,
+                            wl.dtype, wl.k_scale, wl.v_scale, num_threads=num_threads)
+        return out, pool
+    reshape_and_cache(k, v, pool, wl.slot_mapping, wl.dtype)
     out = attention(q, pool, wl.block_tables, wl.query_start_loc, wl.seq_lens, wl.context_lens, wl.scale,
                     wl.dtype, num_threads=num_threads)
     return out, pool

@@ -28,13 +28,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(HERE, "libpa.so")
 BLOCK_SIZE = 16
 
-PA_F32, PA_BF16, PA_I32, PA_I64 = 0, 1, 2, 3
+PA_F32, PA_BF16, PA_I32, PA_I64, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_STRIDE",
     5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP", 8: "PA_ERR_NO_BLOCKS", 9: "PA_ERR_REQUEST",
 }
-EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_attention_workspace_size",
-           "pa_partition_tokens", "pa_status_string", "pa_last_error", "pa_version")
+EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
+           "pa_step_fp8", "pa_attention_workspace_size", "pa_partition_tokens", "pa_status_string", "pa_last_error",
+           "pa_version")
 PROFILE_EXPORTS = ("pa_profile_start", "pa_profile_stop", "pa_profile_kernel", "pa_profile_kernel_name")
 KERNELS = ("kv_write", "decode", "partition_reduce", "prefill_plan", "prefill")
 
@@ -72,7 +73,12 @@ def _load():
     lib.pa_reshape_and_cache.argtypes = [P, P, P, P, P, vp]
     lib.pa_attention.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_float, vp, sz, vp]
     lib.pa_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, ctypes.c_float, vp, sz, vp]
-    for f in ("pa_reshape_and_cache", "pa_attention", "pa_step"):
+    f32 = ctypes.c_float
+    lib.pa_reshape_and_cache_fp8.argtypes = [P, P, P, P, P, f32, f32, vp]
+    lib.pa_attention_fp8.argtypes = [P, P, P, P, P, P, P, P, f32, f32, f32, vp, sz, vp]
+    lib.pa_step_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, f32, f32, f32, vp, sz, vp]
+    for f in ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
+              "pa_step_fp8"):
         getattr(lib, f).restype = ctypes.c_int
     lib.pa_attention_workspace_size.argtypes = [i64] * 6
     lib.pa_attention_workspace_size.restype = sz
@@ -98,7 +104,8 @@ lib = _load()
 def _dtype_code(t) -> int:
     import torch
 
-    codes = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int32: PA_I32, torch.int64: PA_I64}
+    codes = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int32: PA_I32, torch.int64: PA_I64,
+             torch.float8_e4m3fn: PA_FP8_E4M3}
     if t.dtype not in codes:
         raise PAError(2, f"unsupported torch dtype {t.dtype}")
     return codes[t.dtype]
@@ -190,6 +197,41 @@ def step(q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_star
                                 query_start_loc, seq_lens, context_lens)]
     _check(lib.pa_step(*[_ptr(d) for d in ds], ctypes.c_float(scale), ctypes.c_void_p(ws.data_ptr()),
                        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
+    return out
+
+
+def reshape_and_cache_fp8(k, v, key_cache, value_cache, slot_mapping, k_scale: float, v_scale: float) -> None:
+    """KV write into an 8-bit pool (torch.float8_e4m3fn caches): code = nearest(x / scale)."""
+    ds = [describe(x) for x in (k, v, key_cache, value_cache, slot_mapping)]
+    _check(lib.pa_reshape_and_cache_fp8(*[_ptr(d) for d in ds], ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+                                        _stream(key_cache)))
+
+
+def attention_fp8(q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens, scale: float,
+                  k_scale: float, v_scale: float, out=None, workspace=None):
+    import torch
+
+    out = torch.empty_like(q) if out is None else out
+    ws = new_workspace(q, key_cache, block_tables) if workspace is None else workspace
+    ds = [describe(x) for x in (out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens,
+                                context_lens)]
+    _check(lib.pa_attention_fp8(*[_ptr(d) for d in ds], ctypes.c_float(scale), ctypes.c_float(k_scale),
+                                ctypes.c_float(v_scale), ctypes.c_void_p(ws.data_ptr()),
+                                ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
+    return out
+
+
+def step_fp8(q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens, context_lens,
+             scale: float, k_scale: float, v_scale: float, out=None, workspace=None):
+    import torch
+
+    out = torch.empty_like(q) if out is None else out
+    ws = new_workspace(q, key_cache, block_tables) if workspace is None else workspace
+    ds = [describe(x) for x in (out, q, k, v, key_cache, value_cache, slot_mapping, block_tables,
+                                query_start_loc, seq_lens, context_lens)]
+    _check(lib.pa_step_fp8(*[_ptr(d) for d in ds], ctypes.c_float(scale), ctypes.c_float(k_scale),
+                           ctypes.c_float(v_scale), ctypes.c_void_p(ws.data_ptr()),
+                           ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
     return out
 
 

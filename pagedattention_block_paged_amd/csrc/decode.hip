@@ -32,6 +32,7 @@
 //    order (deterministic). Single-partition sequences write the output
 //    directly.
 #include <cstdlib>
+#include <type_traits>
 
 #include "pa_internal.h"
 
@@ -121,6 +122,28 @@ struct BlockRegs {
   uint32_t v[4][Sh::VW];
 };
 
+// One block of an 8-bit (OCP FP8 E4M3) pool in registers, as loaded: K load
+// i of a lane covers row RPI8 i + lane / LPR8, codes 16 (lane % LPR8) ..
+// +15; V: rows 4kg + j, codes VB n .. VB n + VB - 1 (the same elements the
+// bf16 layout gives the lane).
+template <int D>
+struct BlockRegs8 {
+  static constexpr int LPR8 = D / 16;  // lanes per K row (16 codes each)
+  static constexpr int RPI8 = 64 / LPR8;
+  static constexpr int KC8 = D / 64;   // K loads per lane per block
+  static constexpr int VB = D / 16;    // V codes per lane per row
+  static constexpr int VW8 = VB / 4;   // 32-bit words of them
+  uint4 k[KC8];
+  uint32_t v[4][VW8];
+};
+
+// Codes 2 SEL, 2 SEL + 1 of w as two bf16 values (exact: every E4M3 value is
+// a bf16 value), low half first.
+template <bool SEL>
+__device__ inline uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, SEL));
+}
+
 // K: load i of a lane covers row RPI i + lane / LPR, bytes k_off = 16 (lane %
 // LPR) of it (whole 128-byte lines per instruction); V: rows 4kg + j, bytes
 // v_off.
@@ -136,24 +159,75 @@ __device__ inline void load_block(BlockRegs<BF16, D>& r, __amdgpu_buffer_rsrc_t 
   for (int j = 0; j < 4; ++j) load_words<Sh::VW>(vr, v_off, j * vc_sr, r.v[j]);
 }
 
+template <int D>
+__device__ inline void load_block8(BlockRegs8<D>& r, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                   uint32_t k_off, uint32_t kc_sr, uint32_t v_off, uint32_t vc_sr) {
+  using R = BlockRegs8<D>;
+#pragma unroll
+  for (int i = 0; i < R::KC8; ++i)
+    r.k[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off, i * R::RPI8 * kc_sr, kStreamPolicy));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (R::VW8 == 2) {
+      const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off, j * vc_sr, kStreamPolicy));
+      r.v[j][0] = u.x;
+      r.v[j][1] = u.y;
+    } else {
+      r.v[j][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, v_off, j * vc_sr, kStreamPolicy);
+    }
+  }
+}
+
 // Consume one block: scores, online softmax, P.V. `blk` is the block's index
 // within the sequence; rows at or past `end` (the partition's end) are
 // zeroed, and this lane's column sees keys below `lim` only. Lane (kg, n) holds
 // K row n and V rows 4kg..4kg+3 (elements VE*n..VE*n+VE-1) of the block.
 // Accumulators: bf16 path O^T[d = 16t + 4kg + r][head n] in o[t][r];
 // fp32 path O[head 4kg + r][d = VE*n + e] in o[e][r].
-template <bool BF16, int D>
-__device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[DecodeShape<BF16, D>::KC],
+template <bool BF16, int D, bool KV8>
+using RawBlock = std::conditional_t<KV8, BlockRegs8<D>, BlockRegs<BF16, D>>;
+
+template <bool BF16, int D, bool KV8>
+__device__ inline void attend_block(RawBlock<BF16, D, KV8>& raw, const uint4 (&qv)[DecodeShape<BF16, D>::KC],
                                     f32x4 (&o)[DecodeShape<BF16, D>::NACC], float& m_run, float& l_run,
                                     char* tile, int blk, int end, int lim, int lane, float qk_scale) {
   using Sh = DecodeShape<BF16, D>;
   constexpr int KC = Sh::KC, VE = Sh::VE, VW = Sh::VW;
   const int n = lane & 15, kg = lane >> 4;
   // Stage K row-major, then read the MFMA A fragments: lane (kg, n) takes row
-  // n, bytes 64 c + 16 kg (chunk 4c + kg) for k-step c.
+  // n, bytes 64 c + 16 kg (chunk 4c + kg) for k-step c. An 8-bit block is
+  // widened to bf16 on the way: a lane's 16 codes become chunks 2c, 2c + 1.
+  BlockRegs<BF16, D> conv;
+  BlockRegs<BF16, D>& cur = [&]() -> BlockRegs<BF16, D>& {
+    if constexpr (KV8) return conv;
+    else return raw;
+  }();
+  if constexpr (KV8) {
+    using R = BlockRegs8<D>;
 #pragma unroll
-  for (int i = 0; i < KC; ++i)
-    *reinterpret_cast<uint4*>(tile + Sh::kt_off(Sh::RPI * i + lane / Sh::LPR, lane % Sh::LPR)) = cur.k[i];
+    for (int i = 0; i < R::KC8; ++i) {
+      const uint32_t w[4] = {raw.k[i].x, raw.k[i].y, raw.k[i].z, raw.k[i].w};
+      const int row = R::RPI8 * i + lane / R::LPR8, c = 2 * (lane % R::LPR8);
+      *reinterpret_cast<uint4*>(tile + Sh::kt_off(row, c)) =
+          make_uint4(fp8x2_to_bf16x2<false>(w[0]), fp8x2_to_bf16x2<true>(w[0]), fp8x2_to_bf16x2<false>(w[1]),
+                     fp8x2_to_bf16x2<true>(w[1]));
+      *reinterpret_cast<uint4*>(tile + Sh::kt_off(row, c + 1)) =
+          make_uint4(fp8x2_to_bf16x2<false>(w[2]), fp8x2_to_bf16x2<true>(w[2]), fp8x2_to_bf16x2<false>(w[3]),
+                     fp8x2_to_bf16x2<true>(w[3]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < R::VW8; ++w) {
+        conv.v[j][2 * w] = fp8x2_to_bf16x2<false>(raw.v[j][w]);
+        conv.v[j][2 * w + 1] = fp8x2_to_bf16x2<true>(raw.v[j][w]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KC; ++i)
+      *reinterpret_cast<uint4*>(tile + Sh::kt_off(Sh::RPI * i + lane / Sh::LPR, lane % Sh::LPR)) = cur.k[i];
+  }
   __builtin_amdgcn_wave_barrier();
   // scores S^T[token 4kg + r][head n]
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -256,9 +330,10 @@ __device__ inline void attend_block(BlockRegs<BF16, D>& cur, const uint4 (&qv)[D
 // slices of each pool block (one contiguous block of all heads) are read by
 // one workgroup at the same time. Dynamic LDS: per-wave V tiles during the
 // sweep, then each wave's (max, sum, output) for the merge.
-template <bool BF16, int D, int NPF>
+template <bool BF16, int D, int NPF, bool KV8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
                                                                 int hw) {
+  static_assert(!KV8 || BF16, "8-bit pools compute in bf16");
   using Sh = DecodeShape<BF16, D>;
   constexpr int ES = Sh::ES, KC = Sh::KC, VE = Sh::VE;
   extern __shared__ float4 smem4[];
@@ -288,7 +363,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   // Column n is new token n / G at position C + n / G: it sees keys up to there.
   const int C = min(max(a.ctx_lens[s], 0), L);
   const int lim = min(end, C + n / G + 1);
-  const float qk_scale = a.scale * kLog2e;
+  const float qk_scale = a.scale * kLog2e * (KV8 ? a.k_scale : 1.f);
   const int b0 = start / kBlockTokens;
   const int nblk = (end - start + kBlockTokens - 1) / kBlockTokens;
   const int nbw = nblk > phase ? (nblk - phase + wph - 1) / wph : 0;  // blocks b0 + phase + wph i
@@ -307,18 +382,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   const int32_t* bt = bt_all + int64_t(s) * a.bt_row;
   const char* kbase = a.kc + int64_t(g) * a.kc_sh;
   const char* vbase = a.vc + int64_t(g) * a.vc_sh;
-  const uint32_t k_off = static_cast<uint32_t>((lane / Sh::LPR) * a.kc_sr + 16 * (lane % Sh::LPR));
+  // cache element bytes: 1 for an 8-bit pool
+  constexpr int CES = KV8 ? 1 : ES;
+  constexpr int KLPR = KV8 ? BlockRegs8<D>::LPR8 : Sh::LPR;
+  const uint32_t k_off = static_cast<uint32_t>((lane / KLPR) * a.kc_sr + 16 * (lane % KLPR));
   const uint32_t kc_sr = static_cast<uint32_t>(a.kc_sr);
-  const uint32_t v_off = static_cast<uint32_t>(4 * kg * a.vc_sr + VE * ES * n);
-  const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + D * ES);
-  const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + D * ES);
+  const uint32_t v_off = static_cast<uint32_t>(4 * kg * a.vc_sr + VE * CES * n);
+  const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + D * CES);
+  const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + D * CES);
   const uint32_t vc_sr = static_cast<uint32_t>(a.vc_sr);
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
-  auto load = [&](BlockRegs<BF16, D>& r, int i) {
+  auto load = [&](RawBlock<BF16, D, KV8>& r, int i) {
     const uint32_t id = static_cast<uint32_t>(bt[b0 + phase + wph * i]);
     const int64_t pid = id < NB ? int64_t(id) : 0;
-    load_block<BF16, D>(r, block_rsrc(kbase + pid * a.kc_sb, k_rec), block_rsrc(vbase + pid * a.vc_sb, v_rec), k_off,
-                        kc_sr, v_off, vc_sr);
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + pid * a.kc_sb, k_rec);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + pid * a.vc_sb, v_rec);
+    if constexpr (KV8) load_block8<D>(r, kr, vr, k_off, kc_sr, v_off, vc_sr);
+    else load_block<BF16, D>(r, kr, vr, k_off, kc_sr, v_off, vc_sr);
   };
   char* tile = reinterpret_cast<char*>(smem) + wave * Sh::TILE_BYTES;
 
@@ -327,7 +407,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   for (int t = 0; t < Sh::NACC; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  BlockRegs<BF16, D> ring[NPF];
+  RawBlock<BF16, D, KV8> ring[NPF];
 #pragma unroll
   for (int j = 0; j < NPF; ++j)
     if (j < nbw) load(ring[j], j);
@@ -336,8 +416,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     for (int j = 0; j < NPF; ++j) {
       const int ib = i + j;
       if (ib < nbw) {
-        attend_block<BF16, D>(ring[j], qv, o, m_run, l_run, tile, b0 + phase + wph * ib, end, lim, lane,
-                              qk_scale);
+        attend_block<BF16, D, KV8>(ring[j], qv, o, m_run, l_run, tile, b0 + phase + wph * ib, end, lim, lane,
+                                   qk_scale);
         if (ib + NPF < nbw) load(ring[j], ib + NPF);
       }
     }
@@ -391,6 +471,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
       acc.y += sw * x.y;
       acc.z += sw * x.z;
       acc.w += sw * x.w;
+    }
+    if constexpr (KV8) {  // values read back as value(code) * v_scale
+      acc.x *= a.v_scale;
+      acc.y *= a.v_scale;
+      acc.z *= a.v_scale;
+      acc.w *= a.v_scale;
     }
     const int64_t hq = int64_t(hg * hw + hl) * G + h % G;
     const int64_t t = q0 + h / G;  // the column's token
@@ -473,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(AttnArgs a) {
   }
 }
 
-template <bool BF16, int D, int NPF>
+template <bool BF16, int D, int NPF, bool KV8>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   using Sh = DecodeShape<BF16, D>;
   const int hw = decode_heads_per_workgroup(a.Hkv);
@@ -483,13 +569,13 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
   // 16 query heads per KV head at D = 128 need 65 KB for the merge.
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, NPF>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, NPF, KV8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeMaxLds));
   if (attr != hipSuccess) return attr;
   if (lds > kDecodeMaxLds) return hipErrorInvalidValue;
   {
     ProfileScope ps(kDecode, stream);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, NPF>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
+    hipLaunchKernelGGL((decode_kernel<BF16, D, NPF, KV8>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
                        hw);
   }
   hipError_t e = hipGetLastError();
@@ -513,10 +599,13 @@ int prefetch_depth() {
 
 template <bool BF16, int D>
 hipError_t launch_depth(const AttnArgs& a, hipStream_t stream) {
+  if constexpr (BF16) {
+    if (a.kv8) return launch_typed<true, D, 1, true>(a, stream);
+  }
   switch (prefetch_depth()) {
-    case 2: return launch_typed<BF16, D, 2>(a, stream);
-    case 3: return launch_typed<BF16, D, 3>(a, stream);
-    default: return launch_typed<BF16, D, 1>(a, stream);
+    case 2: return launch_typed<BF16, D, 2, false>(a, stream);
+    case 3: return launch_typed<BF16, D, 3, false>(a, stream);
+    default: return launch_typed<BF16, D, 1, false>(a, stream);
   }
 }
 

@@ -9,7 +9,7 @@
 #include <cstdlib>
 #include <string>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.h"
 
 namespace {
@@ -57,6 +57,7 @@ int64_t elem_bytes(int32_t dtype) {
     case PA_BF16: return 2;
     case PA_I32: return 4;
     case PA_I64: return 8;
+    case PA_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -67,6 +68,7 @@ const char* dtype_name(int32_t dtype) {
     case PA_BF16: return "bf16";
     case PA_I32: return "i32";
     case PA_I64: return "i64";
+    case PA_FP8_E4M3: return "fp8_e4m3";
     default: return "?";
   }
 }
@@ -127,10 +129,14 @@ struct CacheShape {
   int32_t dtype;
 };
 
-pa_status check_caches(const pa_tensor* kc, const pa_tensor* vc, CacheShape* cs) {
+pa_status check_caches(const pa_tensor* kc, const pa_tensor* vc, bool fp8, CacheShape* cs) {
   PA_TRY(check_desc(kc, "key_cache", 4));
   PA_TRY(check_desc(vc, "value_cache", 4));
-  if (kc->dtype != PA_F32 && kc->dtype != PA_BF16)
+  if (fp8 && kc->dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "key_cache: dtype %s, expected fp8_e4m3", dtype_name(kc->dtype));
+  if (!fp8 && kc->dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_DTYPE, "key_cache: fp8_e4m3 caches go through the _fp8 calls (they take the scales)");
+  if (!fp8 && kc->dtype != PA_F32 && kc->dtype != PA_BF16)
     return fail(PA_ERR_DTYPE, "key_cache: dtype %s, expected f32 or bf16", dtype_name(kc->dtype));
   PA_TRY(check_dtype(vc, "value_cache", kc->dtype));
   for (int i = 0; i < 4; ++i)
@@ -145,18 +151,33 @@ pa_status check_caches(const pa_tensor* kc, const pa_tensor* vc, CacheShape* cs)
   cs->D = kc->shape[3];
   cs->dtype = kc->dtype;
   if (cs->Hkv < 1 || cs->D < 1) return fail(PA_ERR_SHAPE, "key_cache: empty head dims");
+  if ((cs->D * elem_bytes(cs->dtype)) % 16)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %lld: cache rows must be a multiple of 16 bytes", (long long)cs->D);
+  return PA_OK;
+}
+
+pa_status check_scales(float k_scale, float v_scale) {
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must be finite and > 0 (got %g, %g)", k_scale, v_scale);
   return PA_OK;
 }
 
 pa_status validate_write(const pa_tensor* k, const pa_tensor* v, const pa_tensor* kc, const pa_tensor* vc,
-                         const pa_tensor* slots, pa::WriteArgs* a) {
+                         const pa_tensor* slots, bool fp8, float k_scale, float v_scale, pa::WriteArgs* a) {
   CacheShape cs;
-  PA_TRY(check_caches(kc, vc, &cs));
+  PA_TRY(check_caches(kc, vc, fp8, &cs));
   PA_TRY(check_desc(k, "k", 3));
   PA_TRY(check_desc(v, "v", 3));
   PA_TRY(check_desc(slots, "slot_mapping", 1));
-  PA_TRY(check_dtype(k, "k", cs.dtype));
-  PA_TRY(check_dtype(v, "v", cs.dtype));
+  if (fp8) {
+    PA_TRY(check_scales(k_scale, v_scale));
+    if (k->dtype != PA_F32 && k->dtype != PA_BF16)
+      return fail(PA_ERR_DTYPE, "k: dtype %s, expected f32 or bf16", dtype_name(k->dtype));
+    PA_TRY(check_dtype(v, "v", k->dtype));
+  } else {
+    PA_TRY(check_dtype(k, "k", cs.dtype));
+    PA_TRY(check_dtype(v, "v", cs.dtype));
+  }
   PA_TRY(check_dtype(slots, "slot_mapping", PA_I64));
   const int64_t T = k->shape[0];
   for (int i = 0; i < 3; ++i)
@@ -167,7 +188,7 @@ pa_status validate_write(const pa_tensor* k, const pa_tensor* v, const pa_tensor
   if (slots->shape[0] != T)
     return fail(PA_ERR_SHAPE, "slot_mapping has %lld entries for %lld tokens", (long long)slots->shape[0],
                 (long long)T);
-  const int64_t es = elem_bytes(cs.dtype);
+  const int64_t es = elem_bytes(k->dtype), ces = elem_bytes(cs.dtype);
   if ((cs.D * es) % 16) return fail(PA_ERR_UNSUPPORTED, "head_size %lld: rows must be a multiple of 16 bytes",
                                     (long long)cs.D);
   PA_TRY(check_contig1(slots, "slot_mapping"));
@@ -188,29 +209,35 @@ pa_status validate_write(const pa_tensor* k, const pa_tensor* v, const pa_tensor
   a->k_sh = k->stride[1] * es;
   a->v_st = v->stride[0] * es;
   a->v_sh = v->stride[1] * es;
-  a->kc_sb = kc->stride[0] * es;
-  a->kc_sr = kc->stride[1] * es;
-  a->kc_sh = kc->stride[2] * es;
-  a->vc_sb = vc->stride[0] * es;
-  a->vc_sr = vc->stride[1] * es;
-  a->vc_sh = vc->stride[2] * es;
+  a->kc_sb = kc->stride[0] * ces;
+  a->kc_sr = kc->stride[1] * ces;
+  a->kc_sh = kc->stride[2] * ces;
+  a->vc_sb = vc->stride[0] * ces;
+  a->vc_sr = vc->stride[1] * ces;
+  a->vc_sh = vc->stride[2] * ces;
   a->es = static_cast<int>(es);
+  a->kv8 = fp8;
+  a->k_scale = k_scale;
+  a->v_scale = v_scale;
   return PA_OK;
 }
 
 pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_tensor* kc, const pa_tensor* vc,
                              const pa_tensor* bt, const pa_tensor* qsl, const pa_tensor* sl, const pa_tensor* cl,
-                             float scale, void* ws, size_t ws_bytes, pa::AttnArgs* a) {
+                             float scale, bool fp8, float k_scale, float v_scale, void* ws, size_t ws_bytes,
+                             pa::AttnArgs* a) {
   CacheShape cs;
-  PA_TRY(check_caches(kc, vc, &cs));
+  PA_TRY(check_caches(kc, vc, fp8, &cs));
+  if (fp8) PA_TRY(check_scales(k_scale, v_scale));
+  const int32_t qdt = fp8 ? PA_BF16 : cs.dtype;  // fp8 caches compute in bf16
   PA_TRY(check_desc(out, "out", 3));
   PA_TRY(check_desc(q, "q", 3));
   PA_TRY(check_desc(bt, "block_tables", 2));
   PA_TRY(check_desc(qsl, "query_start_loc", 1));
   PA_TRY(check_desc(sl, "seq_lens", 1));
   PA_TRY(check_desc(cl, "context_lens", 1));
-  PA_TRY(check_dtype(q, "q", cs.dtype));
-  PA_TRY(check_dtype(out, "out", cs.dtype));
+  PA_TRY(check_dtype(q, "q", qdt));
+  PA_TRY(check_dtype(out, "out", qdt));
   PA_TRY(check_dtype(bt, "block_tables", PA_I32));
   PA_TRY(check_dtype(qsl, "query_start_loc", PA_I32));
   PA_TRY(check_dtype(sl, "seq_lens", PA_I32));
@@ -247,7 +274,7 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   if (wl.total > 0 && !ws) return fail(PA_ERR_WORKSPACE, "workspace pointer is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(PA_ERR_WORKSPACE, "workspace not 256-byte aligned");
 
-  const int64_t es = elem_bytes(cs.dtype);
+  const int64_t es = elem_bytes(qdt), ces = elem_bytes(cs.dtype);
   a->out = static_cast<char*>(out->data);
   a->q = static_cast<const char*>(q->data);
   a->kc = static_cast<const char*>(kc->data);
@@ -267,22 +294,25 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   a->out_sh = out->stride[1] * es;
   a->q_st = q->stride[0] * es;
   a->q_sh = q->stride[1] * es;
-  a->kc_sb = kc->stride[0] * es;
-  a->kc_sr = kc->stride[1] * es;
-  a->kc_sh = kc->stride[2] * es;
-  a->vc_sb = vc->stride[0] * es;
-  a->vc_sr = vc->stride[1] * es;
-  a->vc_sh = vc->stride[2] * es;
+  a->kc_sb = kc->stride[0] * ces;
+  a->kc_sr = kc->stride[1] * ces;
+  a->kc_sh = kc->stride[2] * ces;
+  a->vc_sb = vc->stride[0] * ces;
+  a->vc_sr = vc->stride[1] * ces;
+  a->vc_sh = vc->stride[2] * ces;
   a->bt_row = S > 1 ? bt->stride[0] : MB;
   a->scale = scale;
-  a->elem = cs.dtype == PA_F32 ? pa::Elem::F32 : pa::Elem::BF16;
+  a->elem = qdt == PA_F32 ? pa::Elem::F32 : pa::Elem::BF16;
+  a->kv8 = fp8;
+  a->k_scale = fp8 ? k_scale : 1.f;
+  a->v_scale = fp8 ? v_scale : 1.f;
   a->part_tokens = pa::partition_tokens(S, cs.Hkv, MB);
   a->max_parts = (MB * pa::kBlockTokens + a->part_tokens - 1) / a->part_tokens;
   if (MB > (int64_t(1) << 26) || a->max_parts > 65535)
     return fail(PA_ERR_UNSUPPORTED, "block_tables has too many columns (%lld)", (long long)MB);
   if (S * cs.Hkv > int64_t(0x7fffffff)) return fail(PA_ERR_UNSUPPORTED, "too many sequences x KV heads");
   // In-block byte offsets (row within a block, head slice) are 32-bit in the kernels.
-  if (std::max(a->kc_sr, a->vc_sr) * pa::kBlockTokens + D * es > int64_t(0x7fffffff))
+  if (std::max(a->kc_sr, a->vc_sr) * pa::kBlockTokens + D * ces > int64_t(0x7fffffff))
     return fail(PA_ERR_UNSUPPORTED, "cache row stride too large (%lld bytes)", (long long)std::max(a->kc_sr, a->vc_sr));
   char* base = static_cast<char*>(ws);
   a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
@@ -344,7 +374,7 @@ constexpr double kBesideMinDecodeBytes = 4e9;
 // (a sequence on the prefill path has more than 16 / G new tokens), so that
 // batches of decodes alone do not pay for an idle second stream.
 bool prefill_beside_decode(const pa::AttnArgs& a) {
-  if (a.elem != pa::Elem::BF16) return false;
+  if (a.elem != pa::Elem::BF16 || a.kv8) return false;
   const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * 2.0;
   const int64_t G = a.Hq / a.Hkv;
   return kv_bound >= kBesideMinDecodeBytes && a.T - a.S >= pa::kMaxDecodeColumns / G + 1;
@@ -419,24 +449,64 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
 
 extern "C" {
 
-pa_status pa_reshape_and_cache(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
-                               const pa_tensor* value_cache, const pa_tensor* slot_mapping, pa_stream stream) {
+}  // extern "C"
+
+namespace {
+
+pa_status reshape_and_cache_impl(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
+                                 const pa_tensor* value_cache, const pa_tensor* slot_mapping, bool fp8, float k_scale,
+                                 float v_scale, pa_stream stream) {
   pa::WriteArgs a{};
-  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, &a));
+  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, fp8, k_scale, v_scale, &a));
   if (a.T == 0) return ok();
   PA_TRY(hip_status(pa::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv write launch"));
   return ok();
+}
+
+pa_status attention_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
+                         const pa_tensor* value_cache, const pa_tensor* block_tables, const pa_tensor* query_start_loc,
+                         const pa_tensor* seq_lens, const pa_tensor* context_lens, float scale, bool fp8,
+                         float k_scale, float v_scale, void* workspace, size_t workspace_bytes, pa_stream stream) {
+  pa::AttnArgs a{};
+  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
+                            scale, fp8, k_scale, v_scale, workspace, workspace_bytes, &a));
+  PA_TRY(run_attention(a, static_cast<hipStream_t>(stream)));
+  return ok();
+}
+
+pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                    const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                    const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                    const pa_tensor* context_lens, float scale, bool fp8, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, pa_stream stream) {
+  pa::WriteArgs w{};
+  pa::AttnArgs a{};
+  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, fp8, k_scale, v_scale, &w));
+  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
+                            scale, fp8, k_scale, v_scale, workspace, workspace_bytes, &a));
+  if (w.T != a.T)
+    return fail(PA_ERR_SHAPE, "k has %lld tokens, q has %lld", (long long)w.T, (long long)a.T);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
+  PA_TRY(run_attention(a, s));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
+                               const pa_tensor* value_cache, const pa_tensor* slot_mapping, pa_stream stream) {
+  return reshape_and_cache_impl(k, v, key_cache, value_cache, slot_mapping, false, 1.f, 1.f, stream);
 }
 
 pa_status pa_attention(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
                        const pa_tensor* value_cache, const pa_tensor* block_tables,
                        const pa_tensor* query_start_loc, const pa_tensor* seq_lens, const pa_tensor* context_lens,
                        float scale, void* workspace, size_t workspace_bytes, pa_stream stream) {
-  pa::AttnArgs a{};
-  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
-                            scale, workspace, workspace_bytes, &a));
-  PA_TRY(run_attention(a, static_cast<hipStream_t>(stream)));
-  return ok();
+  return attention_impl(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens, scale,
+                        false, 1.f, 1.f, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
@@ -444,17 +514,32 @@ pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, 
                   const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
                   const pa_tensor* context_lens, float scale, void* workspace, size_t workspace_bytes,
                   pa_stream stream) {
-  pa::WriteArgs w{};
-  pa::AttnArgs a{};
-  PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, &w));
-  PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
-                            scale, workspace, workspace_bytes, &a));
-  if (w.T != a.T)
-    return fail(PA_ERR_SHAPE, "k has %lld tokens, q has %lld", (long long)w.T, (long long)a.T);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
-  PA_TRY(run_attention(a, s));
-  return ok();
+  return step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
+                   context_lens, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_reshape_and_cache_fp8(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
+                                   const pa_tensor* value_cache, const pa_tensor* slot_mapping, float k_scale,
+                                   float v_scale, pa_stream stream) {
+  return reshape_and_cache_impl(k, v, key_cache, value_cache, slot_mapping, true, k_scale, v_scale, stream);
+}
+
+pa_status pa_attention_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
+                           const pa_tensor* value_cache, const pa_tensor* block_tables,
+                           const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                           const pa_tensor* context_lens, float scale, float k_scale, float v_scale,
+                           void* workspace, size_t workspace_bytes, pa_stream stream) {
+  return attention_impl(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens, scale,
+                        true, k_scale, v_scale, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_step_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                      const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                      const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                      const pa_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
+                      size_t workspace_bytes, pa_stream stream) {
+  return step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
+                   context_lens, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads, int64_t num_kv_heads,

@@ -50,7 +50,9 @@ struct WriteArgs {
   int64_t k_st, k_sh, v_st, v_sh;        // k/v: token and head strides
   int64_t kc_sb, kc_sr, kc_sh;           // key cache: block, row, head strides
   int64_t vc_sb, vc_sr, vc_sh;           // value cache
-  int es;                                // element bytes
+  int es;                                // element bytes of k and v
+  bool kv8;                              // the caches hold fp8 codes: each element is quantized
+  float k_scale, v_scale;                // fp8 only: code = nearest(x / scale)
 };
 
 // Attention: all tensor strides in bytes except the int32 tables (elements).
@@ -68,7 +70,9 @@ struct AttnArgs {
   int64_t kc_sb, kc_sr, kc_sh, vc_sb, vc_sr, vc_sh;
   int64_t bt_row;  // block-table row stride (elements)
   float scale;
-  Elem elem;
+  Elem elem;              // q, out and the compute path
+  bool kv8;               // the caches hold fp8 codes (elem is bf16)
+  float k_scale, v_scale;  // fp8 only: a cached element reads back as value(code) * scale
   // split-K decode
   int64_t part_tokens;  // tokens per partition (multiple of 16)
   int64_t max_parts;    // partitions per sequence at most: ceil(MB * 16 / part_tokens)

@@ -826,7 +826,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 }
 
 // ---------------------------------------------------------------- fp32 ----
-template <int D, int HW>
+// Also serves 8-bit pools (KV8): q and out are bf16 there, and each K/V
+// element is widened from its E4M3 code (exact) while staging; k_scale
+// joins the score scale and v_scale the output normalisation.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int D, int HW, bool KV8>
 __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
   constexpr int KT = 32;        // keys per LDS stage
   constexpr int KROW = D + 4;   // floats per K tile row
@@ -847,7 +852,8 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
   const int n_hg = G / HW;
   const int64_t total_tiles = a.tile_start[a.S];
   const int64_t n_items = total_tiles * a.Hkv * n_hg;
-  const float c_scale = a.scale * kLog2e;
+  const float c_scale = a.scale * kLog2e * (KV8 ? a.k_scale : 1.f);
+  const float o_scale = KV8 ? a.v_scale : 1.f;
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
 
   for (int64_t item = next_item(a, &item_sh); item < n_items; item = next_item(a, &item_sh)) {
@@ -867,7 +873,11 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
     const int64_t my_pos = C + my_i;
 
     float qf[D / 2];  // Q^T: token col, d = 2 st + hh
-    {
+    if constexpr (KV8) {
+      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q + (q0 + my_i) * a.q_st + h * a.q_sh);
+#pragma unroll
+      for (int st = 0; st < D / 2; ++st) qf[st] = __uint_as_float(static_cast<uint32_t>(qrow[2 * st + hh]) << 16);
+    } else {
       const float* qrow = reinterpret_cast<const float*>(a.q + (q0 + my_i) * a.q_st + h * a.q_sh);
 #pragma unroll
       for (int st = 0; st < D / 2; ++st) qf[st] = qrow[2 * st + hh];
@@ -891,8 +901,17 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
         if (j < kend) {
           const uint32_t id32 = static_cast<uint32_t>(bt[j / kBlockTokens]);
           const int64_t pid = id32 < NB ? int64_t(id32) : 0;
-          kv = *reinterpret_cast<const float4*>(kc + pid * a.kc_sb + (j % kBlockTokens) * a.kc_sr + 16 * c);
-          vv = *reinterpret_cast<const float4*>(vc + pid * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 16 * c);
+          if constexpr (KV8) {  // 4 codes per vector
+            const uint32_t kw = *reinterpret_cast<const uint32_t*>(kc + pid * a.kc_sb + (j % kBlockTokens) * a.kc_sr + 4 * c);
+            const uint32_t vw = *reinterpret_cast<const uint32_t*>(vc + pid * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 4 * c);
+            const f32x2 k01 = __builtin_amdgcn_cvt_pk_f32_fp8(kw, false), k23 = __builtin_amdgcn_cvt_pk_f32_fp8(kw, true);
+            const f32x2 v01 = __builtin_amdgcn_cvt_pk_f32_fp8(vw, false), v23 = __builtin_amdgcn_cvt_pk_f32_fp8(vw, true);
+            kv = make_float4(k01.x, k01.y, k23.x, k23.y);
+            vv = make_float4(v01.x, v01.y, v23.x, v23.y);
+          } else {
+            kv = *reinterpret_cast<const float4*>(kc + pid * a.kc_sb + (j % kBlockTokens) * a.kc_sr + 16 * c);
+            vv = *reinterpret_cast<const float4*>(vc + pid * a.vc_sb + (j % kBlockTokens) * a.vc_sr + 16 * c);
+          }
         }
         *reinterpret_cast<float4*>(ks + key * KROW + 4 * c) = kv;
         vt[(4 * c + 0) * VROW + key] = vv.x;
@@ -940,16 +959,23 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int64_t my_tok = i0 + col;
       if (my_tok < n) {
-        const float inv = 1.f / l_tot;
+        const float inv = o_scale / l_tot;
         char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int d = 32 * dt + 8 * q + 4 * hh;
-            *reinterpret_cast<float4*>(dst + 4 * d) =
-                make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
-                            o[dt][4 * q + 3] * inv);
+            const float4 r = make_float4(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv, o[dt][4 * q + 2] * inv,
+                                         o[dt][4 * q + 3] * inv);
+            if constexpr (KV8) {
+              const bf16x2 lo = {static_cast<__bf16>(r.x), static_cast<__bf16>(r.y)};
+              const bf16x2 hi = {static_cast<__bf16>(r.z), static_cast<__bf16>(r.w)};
+              *reinterpret_cast<uint2*>(dst + 2 * d) =
+                  make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+            } else {
+              *reinterpret_cast<float4*>(dst + 4 * d) = r;
+            }
           }
       }
     }
@@ -979,7 +1005,7 @@ hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, int64_t slots, boo
   return hipGetLastError();
 }
 
-template <bool BF16, int D, int HW>
+template <bool BF16, int D, int HW, bool KV8 = false>
 hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
   const int64_t grid = prefill_slots<BF16, D, HW>(a);
   hipError_t e = launch_plan<BF16, D, HW>(a, stream, grid, beside);
@@ -991,19 +1017,20 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
       hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
                          bf16_lds_bytes<D>(), stream, a, a.block_tables, beside ? 1 : 0);
     } else {
-      hipLaunchKernelGGL((prefill_f32_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
-                         a);
+      hipLaunchKernelGGL((prefill_f32_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
+                         stream, a);
     }
   }
   return hipGetLastError();
 }
 
-template <bool BF16, int D>
+// KV8: an 8-bit pool, attended by the fp32-MFMA kernel (the f32 work layout).
+template <bool BF16, int D, bool KV8 = false>
 hipError_t launch_heads(const AttnArgs& a, hipStream_t stream, bool beside) {
   const int64_t G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_typed<BF16, D, 4>(a, stream, beside);
-  if (G % 2 == 0) return launch_typed<BF16, D, 2>(a, stream, beside);
-  return launch_typed<BF16, D, 1>(a, stream, beside);
+  if (G % 4 == 0) return launch_typed<BF16, D, 4, KV8>(a, stream, beside);
+  if (G % 2 == 0) return launch_typed<BF16, D, 2, KV8>(a, stream, beside);
+  return launch_typed<BF16, D, 1, KV8>(a, stream, beside);
 }
 
 template <int D, int HW>
@@ -1024,6 +1051,8 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
+  if (a.kv8)
+    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, false) : launch_heads<false, 128, true>(a, stream, false);
   const bool bf16 = a.elem == Elem::BF16;
   if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, beside) : launch_heads<false, 64>(a, stream, beside);
   return bf16 ? launch_heads<true, 128>(a, stream, beside) : launch_heads<false, 128>(a, stream, beside);

@@ -4,7 +4,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/pa_profile.h"
+#include "pa_profile.h"
 #include "pa_internal.h"
 
 namespace pa {

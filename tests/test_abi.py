@@ -223,3 +223,49 @@ def test_status_strings():
     for code in range(8):
         assert lib.pa_status_string(code)
     assert lib.pa_version() >= 100
+
+
+FP8 = 4
+
+
+def fp8_case(D=64, NB=32, Hkv=2):
+    c = Case(D=D, NB=NB, Hkv=Hkv)
+    pool_strides = [2 * 16 * Hkv * D, Hkv * D, D, 1]
+    c.kc = desc([NB, 16, Hkv, D], FP8, pool_strides)
+    c.vc = desc([NB, 16, Hkv, D], FP8, pool_strides, data=FAKE + 16 * Hkv * D)
+    return c
+
+
+def attention_fp8(c, ks=0.5, vs=0.25):
+    r = lambda d: ctypes.byref(d)
+    return lib.pa_attention_fp8(r(c.out), r(c.q), r(c.kc), r(c.vc), r(c.bt), r(c.qsl), r(c.sl), r(c.cl),
+                                ctypes.c_float(0.125), ctypes.c_float(ks), ctypes.c_float(vs),
+                                ctypes.c_void_p(c.ws), c.ws_bytes, None)
+
+
+def write_fp8(c, ks=0.5, vs=0.25):
+    r = lambda d: ctypes.byref(d)
+    return lib.pa_reshape_and_cache_fp8(r(c.k), r(c.v), r(c.kc), r(c.vc), r(c.slots), ctypes.c_float(ks),
+                                        ctypes.c_float(vs), None)
+
+
+def test_fp8_pool_validation():
+    # the f32/bf16 calls refuse an 8-bit pool (they carry no scales)
+    c = fp8_case()
+    assert c.attention() == PA_ERR_DTYPE and "_fp8" in err()
+    assert c.write() == PA_ERR_DTYPE
+    # scales must be finite and positive
+    for ks, vs in ((0.0, 1.0), (1.0, -1.0), (float("inf"), 1.0), (float("nan"), 1.0)):
+        assert attention_fp8(fp8_case(), ks, vs) == PA_ERR_SHAPE
+        assert write_fp8(fp8_case(), ks, vs) == PA_ERR_SHAPE
+    # q and out are bf16 over an 8-bit pool; k and v may be f32 or bf16
+    c = fp8_case()
+    c.q = desc([4, 8, 64], F32)
+    assert attention_fp8(c) == PA_ERR_DTYPE
+    c = fp8_case()
+    c.k = desc([0, 2, 64], F32)
+    c.v = desc([0, 2, 64], F32)
+    c.slots = desc([0], I64)
+    assert write_fp8(c) == PA_OK  # accepted; an empty batch launches nothing
+    c.k = desc([0, 2, 64], I32)
+    assert write_fp8(c) == PA_ERR_DTYPE

@@ -1,0 +1,123 @@
+"""8-bit (OCP FP8 E4M3) KV pool on the GPU, through the C ABI's _fp8 calls.
+
+- KV write: the codes the library stores equal the oracle's, bit for bit,
+  for bf16 and f32 inputs that include exact ties, values in the subnormal
+  range, values past the largest code (saturation), zeros of both signs and
+  NaN; every byte the write does not target is unchanged.
+- Attention: random mixes of decodes, short chunks (attended by the decode
+  kernel) and long chunks (the prefill path) at head sizes 64 and 128 and
+  1, 4 and 8 query heads per KV head, and the Llama-3-70B 32k decode batch and
+  the Llama-3-8B mixed step at full size (sampled sequences), against the
+  oracle on the same codes, to the bf16 bounds: the codes widen to bf16 and
+  fp32 exactly, so the pool format adds no error of its own.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import sample_seqs, to_f64
+from parity import assert_within
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import pagedattention_block_paged_amd as lib
+
+    return lib
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def special_rows(T, H, D, dtype, scale, seed):
+    """k/v rows [T, H, D] in the host element type with the edge cases spread in."""
+    rs = np.random.default_rng(seed)
+    x = (rs.normal(0, 1, (T, H, D)) * scale * rs.choice([0.01, 1.0, 30.0], (T, H, D))).astype(np.float32)
+    flat = x.reshape(-1)
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = oracle.fp8_decode(codes)
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    edge = np.concatenate([mids, -mids, vals.astype(np.float32), [600.0, -1e6, np.inf, -np.inf, np.nan, 0.0, -0.0,
+                                                                  2.0 ** -12, -(2.0 ** -10), 464.0, 463.9]])
+    edge = (edge * np.float32(scale)).astype(np.float32)  # values / scale land on the edges
+    n = min(edge.size, flat.size)
+    flat[:n] = edge[:n]
+    rs.shuffle(flat)
+    return W.rng.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("k_scale,v_scale", [(1.0, 1.0), (0.05, 2.5)])
+def test_fp8_write_codes_bit_exact(pa, dtype, k_scale, v_scale):
+    say(f"[fp8 write] {dtype} scales {k_scale} {v_scale}")
+    T, Hkv, D, NB = 200, 2, 128, 40
+    k = special_rows(T, Hkv, D, dtype, k_scale, 1)
+    v = special_rows(T, Hkv, D, dtype, v_scale, 2)
+    rs = np.random.default_rng(3)
+    slots = rs.permutation(NB * 16)[:T].astype(np.int64)
+    slots[::17] = -1  # padding tokens
+    pool = torch.full((NB, 2, 16, Hkv, D), W.rng.CANARY_FP8, dtype=torch.uint8, device="cuda")
+    before = pool.clone()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = lambda a: (torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16) if dtype == "bf16"
+                     else torch.from_numpy(a).cuda())
+    kd, vd = dev(k), dev(v)
+    assert kd.dtype == tdt
+    f8 = pool.view(torch.float8_e4m3fn)
+    pa.reshape_and_cache_fp8(kd, vd, f8[:, 0], f8[:, 1], torch.from_numpy(slots).cuda(), k_scale, v_scale)
+    torch.cuda.synchronize()
+    got = pool.cpu().numpy()
+    ref = before.cpu().numpy()
+    oracle.reshape_and_cache_fp8(k, v, ref, slots, dtype, k_scale, v_scale)
+    assert np.array_equal(got, ref), np.argwhere(got != ref)[:5]
+
+
+MIXES = [  # (Hq, Hkv, D, decode contexts, chunks as (cached, new), seed)
+    (8, 2, 128, [1, 17, 300, 2500], [(0, 70), (1000, 130)], 1),
+    (32, 8, 128, [64, 900, 4100], [(37, 3), (500, 4), (2000, 64)], 2),
+    (8, 8, 64, [5, 333], [(200, 40), (0, 16)], 3),
+    (16, 2, 64, [77, 1025, 3000], [(1, 2), (400, 33)], 4),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MIXES)))
+def test_fp8_random_mixes(pa, idx):
+    Hq, Hkv, D, dec, chunks, seed = MIXES[idx]
+    L = dec + [c + n for c, n in chunks]
+    n = [1] * len(dec) + [n for _, n in chunks]
+    wl = W.with_fp8_pool(W.build_workload(f"fp8mix{idx}", "bf16", Hq, Hkv, D, L, n, seed=seed), 0.4, 0.3)
+    say(f"[fp8 mix {idx}] Hq {Hq} Hkv {Hkv} D {D} L {L} n {n}")
+    out = run_fp8_step(pa, wl)
+    ref, _ = oracle.run_workload(wl)
+    assert_within(out, ref, "bf16", wl.name)
+
+
+def run_fp8_step(pa, wl, rows=None):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = W.q_device(wl, "cuda")
+    k, v = W.new_kv_device(wl, "cuda")
+    pool = W.pool_device(wl, "cuda")
+    assert pool.dtype == torch.float8_e4m3fn
+    out = pa.step_fp8(q, k, v, pool[:, 0], pool[:, 1], t(wl.slot_mapping), t(wl.block_tables),
+                      t(wl.query_start_loc), t(wl.seq_lens), t(wl.context_lens), wl.scale, wl.k_scale, wl.v_scale)
+    torch.cuda.synchronize()
+    out = out if rows is None else out[torch.from_numpy(rows).cuda()]
+    return to_f64(out)
+
+
+@pytest.mark.parametrize("cfg", [4, 3])
+def test_fp8_full_size_sampled(pa, cfg):
+    base = W.config_workload(cfg, hbm_bytes=torch.cuda.get_device_properties(0).total_memory // 2)
+    wl = W.with_fp8_pool(base)
+    say(f"[fp8 cfg {cfg}] {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
+    seqs = sample_seqs(wl, 4)
+    rows = np.concatenate([np.arange(wl.query_start_loc[s], wl.query_start_loc[s + 1]) for s in seqs])
+    out = run_fp8_step(pa, wl, rows)
+    ref, _ = oracle.run_workload(W.sub_workload(wl, seqs))
+    assert_within(out, ref, "bf16", wl.name)

@@ -37,7 +37,7 @@ from . import rng as _rng
 BLOCK_SIZE = 16
 SHARED_IDENT = 1 << 40  # identity of rows in a shared prefix
 STREAM_Q, STREAM_K, STREAM_V = 1, 2, 3
-DTYPE_BYTES = {"f32": 4, "bf16": 2}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 @dataclasses.dataclass
@@ -60,6 +60,19 @@ class Workload:
     seed: int
     canary_block: int  # an unreferenced block; unused table entries point at it
     block_size: int = BLOCK_SIZE
+    # 8-bit pool: kv_dtype "fp8" (OCP E4M3 codes, a cached element reads back as
+    # value(code) * k_scale or * v_scale); "" = the pool holds `dtype`
+    kv_dtype: str = ""
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def pool_dtype(self) -> str:
+        return self.kv_dtype or self.dtype
+
+    @property
+    def kv_elem_bytes(self) -> int:
+        return DTYPE_BYTES[self.pool_dtype]
 
     @property
     def num_seqs(self) -> int:
@@ -83,7 +96,7 @@ class Workload:
 
     @property
     def block_bytes(self) -> int:
-        return 2 * self.block_size * self.num_kv_heads * self.head_size * self.elem_bytes
+        return 2 * self.block_size * self.num_kv_heads * self.head_size * self.kv_elem_bytes
 
     def blocks_used(self, s: int) -> int:
         return -(-int(self.seq_lens[s]) // self.block_size)
@@ -99,13 +112,13 @@ class Workload:
     def kv_read_bytes(self, seqs: Optional[np.ndarray] = None) -> int:
         """K and V bytes attention must read: every key of every sequence once."""
         L = self.seq_lens.astype(np.int64) if seqs is None else self.seq_lens[seqs].astype(np.int64)
-        return int(L.sum()) * 2 * self.num_kv_heads * self.head_size * self.elem_bytes
+        return int(L.sum()) * 2 * self.num_kv_heads * self.head_size * self.kv_elem_bytes
 
     def decode_bytes(self) -> int:
         """Decode roofline bytes: KV read + block-table reads + q read + out write."""
         m = self.decode_mask()
         L = self.seq_lens[m].astype(np.int64)
-        kv = int(L.sum()) * 2 * self.num_kv_heads * self.head_size * self.elem_bytes
+        kv = int(L.sum()) * 2 * self.num_kv_heads * self.head_size * self.kv_elem_bytes
         tables = int((-(-L // self.block_size)).sum()) * 4
         qo = 2 * int(m.sum()) * self.num_q_heads * self.head_size * self.elem_bytes
         return kv + tables + qo
@@ -122,7 +135,7 @@ class Workload:
     def write_bytes(self) -> int:
         """KV-write bytes: read k and v rows, write them into the pool."""
         n = int((self.slot_mapping >= 0).sum())
-        return 2 * 2 * n * self.num_kv_heads * self.head_size * self.elem_bytes
+        return 2 * n * self.num_kv_heads * self.head_size * (self.elem_bytes + self.kv_elem_bytes)
 
 
 def _draw_rng(cfg_id: int, stream: int) -> np.random.Generator:
@@ -268,18 +281,22 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
 
 # --- values -------------------------------------------------------------------
 def _table_np(dtype: str) -> np.ndarray:
+    if dtype == "fp8":
+        return _rng.FP8_CODES
     return _rng.NORMAL_F32 if dtype == "f32" else _rng.NORMAL_BF16
 
 
 def canary_np(dtype: str):
+    if dtype == "fp8":
+        return np.uint8(_rng.CANARY_FP8)
     if dtype == "f32":
         return np.array([_rng.CANARY_F32_BITS], np.uint32).view(np.float32)[0]
     return np.uint16(_rng.CANARY_BF16_BITS)
 
 
 def np_dtype(dtype: str):
-    """Host element type: float32, or uint16 bit patterns for bfloat16."""
-    return np.float32 if dtype == "f32" else np.uint16
+    """Host element type: float32, uint16 bit patterns for bfloat16, uint8 codes for fp8."""
+    return {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}[dtype]
 
 
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -370,9 +387,9 @@ def prior_blocks(wl: Workload):
 
 def pool_host(wl: Workload) -> np.ndarray:
     """Host pool [NB, 2, 16, Hkv, D] before the KV write: cached rows placed, canaries elsewhere."""
-    Hkv, D = wl.num_kv_heads, wl.head_size
-    pool = np.empty((wl.num_blocks, 2, BLOCK_SIZE, Hkv, D), dtype=np_dtype(wl.dtype))
-    pool[...] = canary_np(wl.dtype)
+    Hkv, D, pd = wl.num_kv_heads, wl.head_size, wl.pool_dtype
+    pool = np.empty((wl.num_blocks, 2, BLOCK_SIZE, Hkv, D), dtype=np_dtype(pd))
+    pool[...] = canary_np(pd)
     phys, ident, first, limit = prior_blocks(wl)
     if phys.size == 0:
         return pool
@@ -381,9 +398,9 @@ def pool_host(wl: Workload) -> np.ndarray:
     idn = np.repeat(ident, BLOCK_SIZE)
     valid = (pos < np.repeat(limit, BLOCK_SIZE)).reshape(-1, BLOCK_SIZE)
     for kv, stream in ((0, STREAM_K), (1, STREAM_V)):
-        vals = _rows_np(_rng.stream_key(wl.seed, stream), idn, pos, Hkv * D, wl.dtype)
+        vals = _rows_np(_rng.stream_key(wl.seed, stream), idn, pos, Hkv * D, pd)
         vals = vals.reshape(-1, BLOCK_SIZE, Hkv, D)
-        vals[~valid] = canary_np(wl.dtype)
+        vals[~valid] = canary_np(pd)
         pool[phys, kv] = vals
     return pool
 
@@ -450,6 +467,8 @@ def with_block_tables(wl: Workload, tables, num_blocks: int, canary_block: int) 
 def _table_torch(dtype: str, device):
     import torch
 
+    if dtype == "fp8":
+        return torch.from_numpy(_rng.FP8_CODES.copy()).to(device)
     if dtype == "f32":
         return torch.from_numpy(_rng.NORMAL_F32.copy()).to(device)
     return torch.from_numpy(_rng.NORMAL_BF16.view(np.int16).copy()).to(device).view(torch.bfloat16)
@@ -458,7 +477,7 @@ def _table_torch(dtype: str, device):
 def torch_dtype(dtype: str):
     import torch
 
-    return torch.float32 if dtype == "f32" else torch.bfloat16
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[dtype]
 
 
 def _rows_torch(key, ident, pos, width, table):
@@ -493,6 +512,8 @@ def new_kv_device(wl: Workload, device):
 def canary_torch(dtype: str, device):
     import torch
 
+    if dtype == "fp8":
+        return torch.tensor([_rng.CANARY_FP8], dtype=torch.uint8).to(device)
     if dtype == "f32":
         return torch.tensor([_rng.CANARY_F32_BITS], dtype=torch.int32).view(torch.float32).to(device)
     return torch.tensor([_rng.CANARY_BF16_BITS], dtype=torch.int16).view(torch.bfloat16).to(device)
@@ -502,12 +523,14 @@ def pool_device(wl: Workload, device, *, blocks_per_chunk: int = 8192):
     """Device pool [NB, 2, 16, Hkv, D] before the KV write (same bits as ``pool_host``)."""
     import torch
 
-    Hkv, D = wl.num_kv_heads, wl.head_size
-    pool = torch.empty((wl.num_blocks, 2, BLOCK_SIZE, Hkv, D), dtype=torch_dtype(wl.dtype), device=device)
-    can = canary_torch(wl.dtype, device)
-    fill_canary(pool, wl.dtype)
+    Hkv, D, pd = wl.num_kv_heads, wl.head_size, wl.pool_dtype
+    # an 8-bit pool is filled through a uint8 view (integer indexing) and returned as float8_e4m3fn
+    pool = torch.empty((wl.num_blocks, 2, BLOCK_SIZE, Hkv, D), dtype=torch.uint8 if pd == "fp8" else torch_dtype(pd),
+                       device=device)
+    can = canary_torch(pd, device)
+    fill_canary(pool, pd)
     phys, ident, first, limit = prior_blocks(wl)
-    table = _table_torch(wl.dtype, device)
+    table = _table_torch(pd, device)
     keys = (_rng.stream_key(wl.seed, STREAM_K), _rng.stream_key(wl.seed, STREAM_V))
     r = torch.arange(BLOCK_SIZE, device=device, dtype=torch.int64)
     for a in range(0, phys.size, blocks_per_chunk):
@@ -521,14 +544,16 @@ def pool_device(wl: Workload, device, *, blocks_per_chunk: int = 8192):
             vals = _rows_torch(keys[kv], idn, pos, Hkv * D, table).reshape(-1, BLOCK_SIZE, Hkv, D)
             vals[invalid] = can
             pool[ph, kv] = vals
-    return pool
+    return pool.view(torch.float8_e4m3fn) if pd == "fp8" else pool
 
 
 def fill_canary(t, dtype: str):
     """Fill a tensor with the NaN canary bit pattern (exact bits, in place)."""
     import torch
 
-    if dtype == "f32":
+    if dtype == "fp8":
+        t.view(torch.uint8).fill_(_rng.CANARY_FP8)
+    elif dtype == "f32":
         t.view(torch.int32).fill_(_rng.CANARY_F32_BITS)
     else:
         t.view(torch.int16).fill_(_rng.CANARY_BF16_BITS)
@@ -559,3 +584,11 @@ def token_rows(seed: int, stream: int, idents, positions, heads: int, head_size:
     key = _rng.stream_key(seed, stream)
     rows = _rows_np(key, np.asarray(idents, np.int64), np.asarray(positions, np.int64), heads * head_size, dtype)
     return rows.reshape(-1, heads, head_size)
+
+
+def with_fp8_pool(wl: Workload, k_scale: float = 0.5, v_scale: float = 0.25) -> Workload:
+    """The same workload over an 8-bit pool: q, k, v and out keep ``dtype`` (bf16);
+    cached context is drawn as E4M3 codes; new tokens are quantized by the KV write."""
+    assert wl.dtype == "bf16", "8-bit pools are read by the bf16 compute path"
+    return dataclasses.replace(wl, name=wl.name.replace("_bf16", "") + "_fp8kv", kv_dtype="fp8",
+                               k_scale=float(np.float32(k_scale)), v_scale=float(np.float32(v_scale)))

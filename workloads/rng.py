@@ -106,6 +106,12 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
 NORMAL_F32 = _normal_table_f32()
 NORMAL_BF16 = f32_to_bf16_bits(NORMAL_F32)
 
+# 8-bit (OCP FP8 E4M3) pool contents, drawn as codes from the same 16-bit
+# fields: bit 15 gives the sign, the low byte one of the 56 codes 0x18 .. 0x4F
+# (magnitudes 1/16 .. 3.75). Built from bit fields alone.
+FP8_CODES = (((np.arange(65536) >> 8) & 0x80) | (0x18 + (np.arange(65536) & 0xFF) % 56)).astype(np.uint8)
+CANARY_FP8 = 0x7F
+
 # NaN canaries for pool memory that a correct kernel never reads.
 CANARY_F32_BITS = 0x7FC00000
 CANARY_BF16_BITS = 0x7FC0
