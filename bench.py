@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "decode KV-read GB/s (% HBM peak), mixed-step tokens/s, prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 MFMA
 HEADLINE = 3
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "pagedattention_block_paged_amd", "csrc")
@@ -89,15 +90,26 @@ def kernel_work(wl, dec, pre):
 
     import workloads as W
 
-    es = W.DTYPE_BYTES[wl.dtype]
+    es = W.DTYPE_BYTES[wl.dtype]  # q
     L = wl.seq_lens.astype(np.int64)
     n = wl.query_lens.astype(np.int64)
     C = wl.context_lens.astype(np.int64)
-    kv = int(L[dec].sum()) * 2 * wl.num_kv_heads * wl.head_size * es
+    kv = int(L[dec].sum()) * 2 * wl.num_kv_heads * wl.head_size * wl.kv_elem_bytes
     tables = int((-(-L[dec] // W.BLOCK_SIZE)).sum()) * 4
     q = int(n[dec].sum()) * wl.num_q_heads * wl.head_size * es
     pairs = int((n[pre] * C[pre] + n[pre] * (n[pre] + 1) // 2).sum())  # sum over queries of visible keys
     return kv + tables + q, 4 * wl.head_size * wl.num_q_heads * pairs
+
+
+def run_step(pa, wl, c, out, ws):
+    """One pa_step (pa_step_fp8 over an 8-bit pool) on the device inputs ``c``."""
+    pool = c["pool"]
+    args = (c["q"], c["k"], c["v"], pool[:, 0], pool[:, 1], c["slot_mapping"], c["block_tables"],
+            c["query_start_loc"], c["seq_lens"], c["context_lens"])
+    if wl.kv_dtype == "fp8":
+        pa.step_fp8(*args, wl.scale, wl.k_scale, wl.v_scale, out=out, workspace=ws)
+    else:
+        pa.step(*args, wl.scale, out=out, workspace=ws)
 
 
 def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool = False) -> dict:
@@ -131,8 +143,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
             scratch.fill_(i & 0x7F)
 
     def one_step():
-        pa.step(c["q"], c["k"], c["v"], pool[:, 0], pool[:, 1], c["slot_mapping"], c["block_tables"],
-                c["query_start_loc"], c["seq_lens"], c["context_lens"], wl.scale, out=out, workspace=ws)
+        run_step(pa, wl, c, out, ws)
 
     for i in range(warmup):
         evict(i)
@@ -199,6 +210,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         "num_kv_heads": wl.num_kv_heads,
         "head_size": wl.head_size,
         "dtype": wl.dtype,
+        "kv_dtype": wl.pool_dtype,
         "pool_blocks": wl.num_blocks,
         "partition_tokens": pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_blocks),
         "ms_per_step": ms,
@@ -222,7 +234,9 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
     if flops and "prefill" in kern:
         p = alone["prefill_ms"] if alone else kern["prefill"]["avg_ms"]
         r["prefill_tflops"] = flops / (p * 1e-3) / 1e12
-        r["prefill_mfma_frac"] = r["prefill_tflops"] / BF16_PEAK_TFLOPS
+        # an 8-bit pool's prefill runs on the fp32 matrix cores
+        r["prefill_mfma_peak"] = FP32_MFMA_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+        r["prefill_mfma_frac"] = r["prefill_tflops"] / r["prefill_mfma_peak"]
         if alone:
             r["prefill_alone"] = alone
             r["prefill_in_step_ms"] = kern["prefill"]["avg_ms"]
@@ -250,14 +264,13 @@ def measure_prefill_alone(pa, wl, c, pre_set, steps, evict):
         "block_tables": c["block_tables"][idx].contiguous(), "query_start_loc": sub_qsl.cuda(),
         "seq_lens": c["seq_lens"][idx].contiguous(), "context_lens": c["context_lens"][idx].contiguous(),
     }
-    pool = c["pool"]
+    sub["pool"] = c["pool"]
     out = torch.empty_like(sub["q"])
-    ws = pa.new_workspace(sub["q"], pool[:, 0], sub["block_tables"])
+    ws = pa.new_workspace(sub["q"], sub["pool"][:, 0], sub["block_tables"])
 
     def one():
         # the KV write rewrites the chunks' rows with the values they already hold
-        pa.step(sub["q"], sub["k"], sub["v"], pool[:, 0], pool[:, 1], sub["slot_mapping"], sub["block_tables"],
-                sub["query_start_loc"], sub["seq_lens"], sub["context_lens"], wl.scale, out=out, workspace=ws)
+        run_step(pa, wl, sub, out, ws)
 
     for i in range(2):
         evict(i)
@@ -425,13 +438,21 @@ def kernel_traffic(kernel: str, workload: str):
     return rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"]
 
 
+def prefill_timing_note(head: dict) -> str:
+    if not head.get("prefill_alone"):
+        return "in the step"
+    where = ("after the decode kernel, on the fp32-MFMA kernel of 8-bit pools" if head.get("kv_dtype") == "fp8"
+             else "beside the decode on a few CUs, hidden behind it")
+    return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
-    ap.add_argument("--secondary", default="2,4,5,6", help="other workloads to measure, or 'none'")
+    ap.add_argument("--secondary", default="2,4,5,6,7,8", help="other workloads to measure, or 'none'")
     ap.add_argument("--secondary-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-manager", action="store_true",
@@ -523,14 +544,12 @@ def main():
             "kernel": "prefill",
             "bound": "mfma",
             "achieved": pre,
-            "peak": BF16_PEAK_TFLOPS,
+            "peak": head.get("prefill_mfma_peak", BF16_PEAK_TFLOPS),
             "unit": "TFLOP/s",
-            "frac": pre / BF16_PEAK_TFLOPS,
+            "frac": pre / head.get("prefill_mfma_peak", BF16_PEAK_TFLOPS),
             "traffic": kernel_traffic("prefill", head["workload"]),
             "algorithmic_flops": head["prefill_flops"],
-            "timed": ("the step's prefill chunks alone; in the step the kernel runs beside the decode "
-                      f"({head['prefill_in_step_ms']:.3f} ms on a few CUs, hidden behind it)")
-            if head.get("prefill_alone") else "in the step",
+            "timed": prefill_timing_note(head),
         },
         "cpu_baseline": cpu,
         "host_kv_manager": mgr,

@@ -235,6 +235,8 @@ CONFIG_NAMES = {
     4: "llama3_70b_32k_decode_bf16",
     5: "prefix_shared_decode_bf16",
     6: "llama3_8b_spec_verify_bf16",
+    7: "llama3_70b_32k_decode_fp8kv",
+    8: "llama3_8b_mixed_prefill_decode_fp8kv",
 }
 
 DEFAULT_HBM_BYTES = 288 * (1 << 30)
@@ -244,8 +246,15 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
     """The benchmark/parity workloads (decode lengths include the new token).
 
     1-5 are the path's configurations; 6 is speculative-decode verification
-    (short multi-token queries over long contexts)."""
+    (short multi-token queries over long contexts); 7 and 8 are the 70B 32k
+    decode and the 8B mixed step over an 8-bit (fp8) KV pool (the 70B pool
+    again ~60% of HBM, in 32 KiB blocks)."""
     name = CONFIG_NAMES[cfg]
+    if cfg == 7:
+        hbm = DEFAULT_HBM_BYTES if hbm_bytes is None else int(hbm_bytes)
+        return with_fp8_pool(config_workload(4, hbm_bytes=2 * hbm))
+    if cfg == 8:
+        return with_fp8_pool(config_workload(3))
     r = _draw_rng(cfg, 0)
     if cfg == 1:
         L = np.array([1, 17, 50, 100])
