@@ -441,8 +441,8 @@ def kernel_traffic(kernel: str, workload: str):
 def prefill_timing_note(head: dict) -> str:
     if not head.get("prefill_alone"):
         return "in the step"
-    where = ("after the decode kernel, on the fp32-MFMA kernel of 8-bit pools" if head.get("kv_dtype") == "fp8"
-             else "beside the decode on a few CUs, hidden behind it")
+    where = ("beside the decode on a share of the CUs (the fp32-MFMA kernel of 8-bit pools)"
+             if head.get("kv_dtype") == "fp8" else "beside the decode on a few CUs, hidden behind it")
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 

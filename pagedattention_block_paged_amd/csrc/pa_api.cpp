@@ -374,8 +374,9 @@ constexpr double kBesideMinDecodeBytes = 4e9;
 // (a sequence on the prefill path has more than 16 / G new tokens), so that
 // batches of decodes alone do not pay for an idle second stream.
 bool prefill_beside_decode(const pa::AttnArgs& a) {
-  if (a.elem != pa::Elem::BF16 || a.kv8) return false;
-  const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * 2.0;
+  if (a.elem != pa::Elem::BF16) return false;
+  const double kv_bytes = a.kv8 ? 1.0 : 2.0;
+  const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * kv_bytes;
   const int64_t G = a.Hq / a.Hkv;
   return kv_bound >= kBesideMinDecodeBytes && a.T - a.S >= pa::kMaxDecodeColumns / G + 1;
 }

@@ -75,10 +75,19 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 
 // Cost model for running the prefill beside the decode kernel (measured on
-// MI355X at head size 128): a prefill workgroup computes about 4.7 TFLOP/s
-// and spends about 6 us per item outside its key loop; the decode reads
-// about 6.6 TB/s over all 256 CUs.
+// MI355X at head size 128): a CU of the bf16 prefill kernel computes about
+// 4.7 TFLOP/s (the fp32-MFMA kernel that serves 8-bit pools about 0.36) and
+// spends about 6 us per item outside its key loop; the decode reads about
+// 6.6 TB/s over all 256 CUs.
 constexpr float kPrefillFlopPerCuUs = 4.7e6f;
+constexpr float kPrefillF32FlopPerCuUs = 0.36e6f;
+constexpr int kThreadsPerCuF32 = 4 * kThreads;  // the fp32 kernel runs 4 workgroups per CU
+// CUs given to the prefill beside the decode: ratio * 256 * prefill work /
+// (prefill + decode work). 2 for the bf16 kernel (its share then finishes in
+// about half the decode's time, and the HBM-bound decode barely notices the
+// CUs it lost); the decode of an 8-bit pool reads half the bytes and notices
+// more, so the slower fp32 kernel gets a smaller share.
+constexpr float kBesideRatioF32 = 1.0f;
 constexpr float kPrefillItemCuUs = 6.0f;
 constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
 
@@ -93,7 +102,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
                                                     int64_t bt_row, int64_t S, int64_t T, int64_t MB,
                                                     int64_t G, int qtile, int64_t Hq, int64_t D,
                                                     int64_t kv_token_bytes, int items_per_tile, int slots,
-                                                    int beside, int32_t* tile_start, int32_t* tile_order,
+                                                    int beside, float flop_per_cu_us, int wg_per_cu, float ratio,
+                                                    int32_t* tile_start, int32_t* tile_order,
                                                     int32_t* counter) {
   __shared__ int32_t part[1024];
   __shared__ float red_dec[1024], red_pre[1024];
@@ -172,13 +182,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
   if (tid == 1023) tile_start[S] = total;
   if (tid == 0) {
     counter[0] = 0;
-    const float pre = red_pre[0] * 4.f * static_cast<float>(D * Hq) / kPrefillFlopPerCuUs +
+    const float pre = red_pre[0] * 4.f * static_cast<float>(D * Hq) / flop_per_cu_us +
                       static_cast<float>(total) * items_per_tile * kPrefillItemCuUs;
     const float dec = red_dec[0] * static_cast<float>(kv_token_bytes) / kDecodeBytePerCuUs;
     int active = 0;
     if (total > 0)
-      active = (beside && dec > 0.f) ? static_cast<int>(ceilf(2.f * 256.f * pre / (pre + dec))) : slots;
-    counter[1] = min(max(active, total > 0 ? 1 : 0), slots);
+      active = (beside && dec > 0.f) ? static_cast<int>(ceilf(ratio * 256.f * pre / (pre + dec))) : slots;
+    counter[1] = min(max(active * wg_per_cu, total > 0 ? 1 : 0), slots);  // CUs -> workgroups
   }
   if (total > kMaxSortedTiles) return;  // uniform: tiles go in sequence order
   __syncthreads();
@@ -832,7 +842,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int HW, bool KV8>
-__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a, int beside) {
+  // beside the decode kernel only the plan kernel's share of workgroups take items
+  if (beside && static_cast<int>(blockIdx.x) >= min(a.work_counter[1], static_cast<int>(gridDim.x))) return;
   constexpr int KT = 32;        // keys per LDS stage
   constexpr int KROW = D + 4;   // floats per K tile row
   constexpr int VROW = KT + 4;  // floats per V^T tile row
@@ -999,8 +1011,11 @@ hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, int64_t slots, boo
   constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
   ProfileScope ps(kPlan, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.block_tables,
-                     a.bt_row, a.S, a.T, a.MB, a.Hq / a.Hkv, QTB, a.Hq, a.D, 2 * a.Hkv * a.D * (BF16 ? 2 : 4),
+                     a.bt_row, a.S, a.T, a.MB, a.Hq / a.Hkv, QTB, a.Hq, a.D,
+                     2 * a.Hkv * a.D * (a.kv8 ? 1 : (a.elem == Elem::BF16 ? 2 : 4)),
                      static_cast<int>(a.Hkv * (a.Hq / a.Hkv / HW)), static_cast<int>(slots), beside ? 1 : 0,
+                     BF16 ? kPrefillFlopPerCuUs : kPrefillF32FlopPerCuUs, BF16 ? 1 : kThreadsPerCuF32 / kThreads,
+                     BF16 ? 2.f : kBesideRatioF32,
                      a.tile_start, a.tile_order, a.work_counter);
   return hipGetLastError();
 }
@@ -1018,7 +1033,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
                          bf16_lds_bytes<D>(), stream, a, a.block_tables, beside ? 1 : 0);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                         stream, a);
+                         stream, a, beside ? 1 : 0);
     }
   }
   return hipGetLastError();
@@ -1052,7 +1067,7 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
   }();
   if (lds_ok != hipSuccess) return lds_ok;
   if (a.kv8)
-    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, false) : launch_heads<false, 128, true>(a, stream, false);
+    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, beside) : launch_heads<false, 128, true>(a, stream, beside);
   const bool bf16 = a.elem == Elem::BF16;
   if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, beside) : launch_heads<false, 64>(a, stream, beside);
   return bf16 ? launch_heads<true, 128>(a, stream, beside) : launch_heads<false, 128>(a, stream, beside);
