@@ -234,8 +234,10 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
     if flops and "prefill" in kern:
         p = alone["prefill_ms"] if alone else kern["prefill"]["avg_ms"]
         r["prefill_tflops"] = flops / (p * 1e-3) / 1e12
-        # an 8-bit pool's prefill runs on the fp32 matrix cores
-        r["prefill_mfma_peak"] = FP32_MFMA_PEAK_TFLOPS if wl.kv_dtype == "fp8" else BF16_PEAK_TFLOPS
+        # an 8-bit pool's prefill runs on the bf16 matrix cores at head size
+        # 128 (codes widened on their way into LDS), on the fp32 ones at 64
+        r["prefill_mfma_peak"] = (FP32_MFMA_PEAK_TFLOPS if wl.kv_dtype == "fp8" and wl.head_size != 128
+                                  else BF16_PEAK_TFLOPS)
         r["prefill_mfma_frac"] = r["prefill_tflops"] / r["prefill_mfma_peak"]
         if alone:
             r["prefill_alone"] = alone
@@ -441,8 +443,7 @@ def kernel_traffic(kernel: str, workload: str):
 def prefill_timing_note(head: dict) -> str:
     if not head.get("prefill_alone"):
         return "in the step"
-    where = ("beside the decode on a share of the CUs (the fp32-MFMA kernel of 8-bit pools)"
-             if head.get("kv_dtype") == "fp8" else "beside the decode on a few CUs, hidden behind it")
+    where = "beside the decode on a few CUs, hidden behind it"
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 

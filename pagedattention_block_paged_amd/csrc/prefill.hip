@@ -49,6 +49,8 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) const uint4 lds_u4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
@@ -355,7 +357,7 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
 // the two kinds of access are independent; handing the compiler two distinct
 // restrict pointers lets it see that (otherwise it waits for every load in
 // flight before each LDS read).
-template <int D, int HW>
+template <int D, int HW, bool KV8>
 __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const AttnArgs& a,
                                                                         const int32_t* __restrict__ bt_all,
                                                                         lds_char* __restrict__ dma,
@@ -380,8 +382,10 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
   const int n_hg = G / HW;
   const int64_t total_tiles = a.tile_start[a.S];
   const int64_t n_items = total_tiles * a.Hkv * n_hg;
-  const float c_scale = a.scale * kLog2e;
+  // an 8-bit pool reads back as value(code) * k_scale: the factor joins Q's scale
+  const float c_scale = a.scale * kLog2e * (KV8 ? a.k_scale : 1.f);
   const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
+  static_assert(!KV8 || D == 128, "8-bit pools take this kernel at head size 128");
 
   // Per-lane fragment addresses in stage 0 (K: slice 0; V: rows of slice 0).
   // The swizzle term depends only on the row modulo 16, which no slice or
@@ -420,6 +424,14 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     dv[i] = static_cast<uint32_t>((r % kBlockTokens) * a.vc_sr + 16 * c);
   }
   auto blk_of = [&](int i) { return (64 * (wave + kPWaves * i) / CPR) / kBlockTokens; };
+  // 8-bit pool: lane (wave, lane) fetches the 16 codes 16 c8 .. +15 of tile
+  // row r8 (8 lanes per 128-code row; a wave's 8 rows lie in block wave / 2 of
+  // the tile) and writes them widened to bf16 as chunks 2 c8, 2 c8 + 1 of that
+  // row, the layout the fragment reads expect.
+  const int r8 = (64 * wave + lane) / 8, c8 = lane % 8;
+  const uint32_t dk8 = static_cast<uint32_t>((r8 % kBlockTokens) * a.kc_sr + 16 * c8);
+  const uint32_t dv8 = static_cast<uint32_t>((r8 % kBlockTokens) * a.vc_sr + 16 * c8);
+  const uint32_t wk8 = 16u * Tl::chunk(r8, 2 * c8), wk8b = 16u * Tl::chunk(r8, 2 * c8 + 1);
 
   // A workgroup's first item is its own index (items are ranked longest
   // first, so this is the first round of a longest-first assignment); later
@@ -456,8 +468,9 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     const char* vc = a.vc + g * a.vc_sh;
     const int last_blk = (kend - 1) / kBlockTokens;
     // bytes of one block's head slice, from its first row
-    const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + a.D * 2);
-    const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + a.D * 2);
+    constexpr int CES = KV8 ? 1 : 2;  // cache element bytes
+    const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + a.D * CES);
+    const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + a.D * CES);
     int32_t ids[DPW];  // block ids of the next tile to load (scalar)
     auto load_ids = [&](int t) {
 #pragma unroll
@@ -475,6 +488,47 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         const int jj = j & 3;
         ids[i] = jj == 0 ? q.x : jj == 1 ? q.y : jj == 2 ? q.z : q.w;
       }
+    };
+    // 8-bit pool: the codes of two tiles in flight in registers (slot t % 2),
+    // and the block id of the next tile to load (scalar).
+    uint4 rk8[2], rv8[2];
+    int32_t id8 = 0;
+    auto load_id8 = [&](int t) { id8 = bt[min(t * (KT / kBlockTokens) + wave / 2, last_blk)]; };
+    auto first_id8 = [&](int t) {
+      if (!tr.ranked) return load_id8(t);
+      const int j = min(t * (KT / kBlockTokens) + wave / 2, last_blk);
+      const int4 q = j < 4 ? tr.ids_lo : tr.ids_hi;
+      const int jj = j & 3;
+      id8 = jj == 0 ? q.x : jj == 1 ? q.y : jj == 2 ? q.z : q.w;
+    };
+    auto load_regs8 = [&](int t, int slot) {
+      const uint32_t u = static_cast<uint32_t>(id8);
+      const int64_t pid = u < NB ? int64_t(u) : 0;
+      uint32_t ok = dk8, ov = dv8;
+      if (t == nkt - 1 && t * KT + r8 >= kend) ok = ov = 0x80000000u;  // past the keys: zeros
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kc + pid * a.kc_sb), 0, static_cast<int>(k_rec), kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vc + pid * a.vc_sb), 0, static_cast<int>(v_rec), kBufferFlags);
+      rk8[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, ok, 0, 0));
+      rv8[slot] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, ov, 0, 0));
+    };
+    // Codes 2 SEL, 2 SEL + 1 of w as bf16 (exact).
+    auto widen2 = [](uint32_t w, auto sel_c) {
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, decltype(sel_c)::value));
+    };
+    auto write_regs8 = [&](int slot, uint32_t stage_off) {
+      using f = std::false_type;
+      using t = std::true_type;
+      const uint4 k = rk8[slot], v = rv8[slot];
+      *reinterpret_cast<lds_u32x4*>(dma + stage_off + wk8) =
+          u32x4{widen2(k.x, f{}), widen2(k.x, t{}), widen2(k.y, f{}), widen2(k.y, t{})};
+      *reinterpret_cast<lds_u32x4*>(dma + stage_off + wk8b) =
+          u32x4{widen2(k.z, f{}), widen2(k.z, t{}), widen2(k.w, f{}), widen2(k.w, t{})};
+      *reinterpret_cast<lds_u32x4*>(dma + V0 + stage_off + wk8) =
+          u32x4{widen2(v.x, f{}), widen2(v.x, t{}), widen2(v.y, f{}), widen2(v.y, t{})};
+      *reinterpret_cast<lds_u32x4*>(dma + V0 + stage_off + wk8b) =
+          u32x4{widen2(v.z, f{}), widen2(v.z, t{}), widen2(v.w, f{}), widen2(v.w, t{})};
     };
     // Rows at or past kend (only in the last tile) read past the resource and
     // land as zeros; their block index is clamped to a block the tile needs.
@@ -724,23 +778,47 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 
     if (nkt > 0) {
       // Prologue: tiles 0 and 1 in flight, wait for tile 0 (and the Q loads).
-      first_ids(0);
-      load_tile(0, 0);
-      if (nkt > 1) {
-        first_ids(1);
-        load_tile(1, TB);
-        wait_vmem<2 * DPW>();
+      // An 8-bit pool's tile goes through registers: its codes are widened
+      // into the stage just before the barrier that publishes it.
+      if constexpr (KV8) {
+        first_id8(0);
+        load_regs8(0, 0);
+        if (nkt > 1) {
+          first_id8(1);
+          load_regs8(1, 1);
+          wait_vmem<2>();
+        } else {
+          wait_vmem<0>();
+        }
+        write_regs8(0, 0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       } else {
-        wait_vmem<0>();
+        first_ids(0);
+        load_tile(0, 0);
+        if (nkt > 1) {
+          first_ids(1);
+          load_tile(1, TB);
+          wait_vmem<2 * DPW>();
+        } else {
+          wait_vmem<0>();
+        }
       }
       raw_barrier();
       // Claim point for short items: after the last tile's loads went out.
       if (nkt <= 2) claim();
       if (nkt > 2) {
-        load_ids(2);
-        load_tile(2, 2 * TB);
+        if constexpr (KV8) {
+          load_id8(2);
+          load_regs8(2, 0);
+        } else {
+          load_ids(2);
+          load_tile(2, 2 * TB);
+        }
       }
-      if (nkt > 3) load_ids(3);
+      if (nkt > 3) {
+        if constexpr (KV8) load_id8(3);
+        else load_ids(3);
+      }
       // The Q loads have landed (they were issued before tile 0). Passing the
       // fragments through an empty asm tells the compiler so; otherwise it
       // cannot prove it inside the tile loop and waits there on the vector-
@@ -759,17 +837,27 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         // Wave 0's claim (issued after the last tile's loads) may stay in
         // flight through the last tile.
         if (u + 1 < nkt)
-          wait_vmem<2 * DPW>();
+          wait_vmem<KV8 ? 2 : 2 * DPW>();
         else if (wave == 0)
           wait_vmem<1>();
         else
           wait_vmem<0>();
+        if constexpr (KV8) {  // tile u's codes (slot u % 2) into its stage, published by the barrier
+          write_regs8(S % 2, kst);
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
         raw_barrier();
-        if (u + 2 < nkt) load_tile(u + 2, nst);
+        if (u + 2 < nkt) {
+          if constexpr (KV8) load_regs8(u + 2, S % 2);
+          else load_tile(u + 2, nst);
+        }
         if (u + 2 == nkt) claim();
         step(yes{}, 2 * u - 1, kst, vst);
         step(yes{}, 2 * u, kst + HALF, vst + HALF);
-        if (u + 3 < nkt) load_ids(u + 3);
+        if (u + 3 < nkt) {
+          if constexpr (KV8) load_id8(u + 3);
+          else load_ids(u + 3);
+        }
       };
       static_assert(Tl::STAGES == 4, "the tile loop is unrolled over four stages");
       for (int u0 = 0; u0 < nkt; u0 += 4) {
@@ -792,7 +880,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const int my_tok = i0 + col;
       if (my_tok < n) {
-        const float inv = 1.f / l_tot;
+        const float inv = (KV8 ? a.v_scale : 1.f) / l_tot;
         char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
         // lane holds O^T[d = 32 dt + 8 q + 4 hh + r][token col]
 #pragma unroll
@@ -819,7 +907,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 // prefill runs beside the decode kernel (`beside`), only the first
 // counter[1] workgroups (the plan kernel's share of the CUs) take items; the
 // others exit at once and leave their CUs to the decode.
-template <int D, int HW>
+template <int D, int HW, bool KV8>
 __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
                                                                  int beside) {
   const int active = beside ? min(a.work_counter[1], static_cast<int>(gridDim.x)) : static_cast<int>(gridDim.x);
@@ -832,7 +920,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   // distinct values (identical arguments would defeat the restrict hint).
   uint32_t zero = 0;
   asm volatile("" : "+s"(zero));
-  prefill_bf16_items<D, HW>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh, blockIdx.x, active);
+  prefill_bf16_items<D, HW, KV8>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh, blockIdx.x, active);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -1029,7 +1117,7 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, HW>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
                          bf16_lds_bytes<D>(), stream, a, a.block_tables, beside ? 1 : 0);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
@@ -1048,10 +1136,10 @@ hipError_t launch_heads(const AttnArgs& a, hipStream_t stream, bool beside) {
   return launch_typed<BF16, D, 1, KV8>(a, stream, beside);
 }
 
-template <int D, int HW>
+template <int D, int HW, bool KV8 = false>
 hipError_t allow_lds() {
   // The four bf16 K and V stages take 128 KB of dynamic LDS at D = 128.
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, HW>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_bf16_kernel<D, HW, KV8>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bf16_lds_bytes<D>()));
 }
 
@@ -1061,13 +1149,16 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
   static const hipError_t lds_ok = [] {
     hipError_t e = hipSuccess;
     for (hipError_t r : {allow_lds<64, 1>(), allow_lds<64, 2>(), allow_lds<64, 4>(), allow_lds<128, 1>(),
-                         allow_lds<128, 2>(), allow_lds<128, 4>()})
+                         allow_lds<128, 2>(), allow_lds<128, 4>(), allow_lds<128, 1, true>(),
+                         allow_lds<128, 2, true>(), allow_lds<128, 4, true>()})
       if (r != hipSuccess) e = r;
     return e;
   }();
   if (lds_ok != hipSuccess) return lds_ok;
+  // 8-bit pools: the bf16-MFMA kernel widens the codes at head size 128; the
+  // fp32-MFMA kernel serves head size 64
   if (a.kv8)
-    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, beside) : launch_heads<false, 128, true>(a, stream, beside);
+    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, beside) : launch_heads<true, 128, true>(a, stream, beside);
   const bool bf16 = a.elem == Elem::BF16;
   if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, beside) : launch_heads<false, 64>(a, stream, beside);
   return bf16 ? launch_heads<true, 128>(a, stream, beside) : launch_heads<false, 128>(a, stream, beside);

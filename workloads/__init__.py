@@ -595,7 +595,7 @@ def token_rows(seed: int, stream: int, idents, positions, heads: int, head_size:
     return rows.reshape(-1, heads, head_size)
 
 
-def with_fp8_pool(wl: Workload, k_scale: float = 0.5, v_scale: float = 0.25) -> Workload:
+def with_fp8_pool(wl: Workload, k_scale: float = 1.0, v_scale: float = 1.0) -> Workload:
     """The same workload over an 8-bit pool: q, k, v and out keep ``dtype`` (bf16);
     cached context is drawn as E4M3 codes; new tokens are quantized by the KV write."""
     assert wl.dtype == "bf16", "8-bit pools are read by the bf16 compute path"

@@ -107,9 +107,21 @@ NORMAL_F32 = _normal_table_f32()
 NORMAL_BF16 = f32_to_bf16_bits(NORMAL_F32)
 
 # 8-bit (OCP FP8 E4M3) pool contents, drawn as codes from the same 16-bit
-# fields: bit 15 gives the sign, the low byte one of the 56 codes 0x18 .. 0x4F
-# (magnitudes 1/16 .. 3.75). Built from bit fields alone.
-FP8_CODES = (((np.arange(65536) >> 8) & 0x80) | (0x18 + (np.arange(65536) & 0xFF) % 56)).astype(np.uint8)
+# fields, shaped like N(0, 1): bit 15 is the sign, bits 8..10 the mantissa,
+# and the low byte picks the exponent field with about the probability that
+# |N(0, 1)| falls in that power-of-two band ([2, 4): 12/256, [1, 2): 70/256,
+# [1/2, 1): 77/256, ... down to the subnormals). Built from bit fields and a
+# fixed table of thresholds, with no rounding arithmetic.
+_FP8_EXP_THRESHOLDS = np.array([12, 82, 159, 204, 229, 242, 249, 253, 256])  # exponent fields 8, 7, ..., 0
+
+
+def _fp8_codes() -> np.ndarray:
+    u = np.arange(65536)
+    e = 8 - np.searchsorted(_FP8_EXP_THRESHOLDS, u & 0xFF, side="right")
+    return (((u >> 8) & 0x80) | (e << 3) | ((u >> 8) & 7)).astype(np.uint8)
+
+
+FP8_CODES = _fp8_codes()
 CANARY_FP8 = 0x7F
 
 # NaN canaries for pool memory that a correct kernel never reads.
