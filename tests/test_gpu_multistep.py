@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads as W
 from oracle.dense import dense_attention
 from parity import assert_within
@@ -56,14 +57,20 @@ def requests():
 
 
 class Driver:
-    def __init__(self, pa, caching, dtype, Hq, Hkv, D, num_blocks=96, budget=48):
+    def __init__(self, pa, caching, dtype, Hq, Hkv, D, num_blocks=96, budget=48, fp8_scales=None):
         from pagedattention_block_paged_amd.kv_manager import KVCacheManager
 
         self.pa, self.dtype, self.Hq, self.Hkv, self.D, self.budget = pa, dtype, Hq, Hkv, D, budget
+        self.fp8 = fp8_scales  # (k_scale, v_scale) for an 8-bit pool, else None
         self.mgr = KVCacheManager(num_blocks, 16, caching)
-        tdt = W.torch_dtype(dtype)
-        self.pool = torch.empty((num_blocks, 2, 16, Hkv, D), dtype=tdt, device="cuda")
-        W.fill_canary(self.pool, dtype)
+        pool_dtype = "fp8" if self.fp8 else dtype
+        if self.fp8:
+            self.pool = torch.empty((num_blocks, 2, 16, Hkv, D), dtype=torch.uint8, device="cuda")
+            W.fill_canary(self.pool, "fp8")
+            self.pool = self.pool.view(torch.float8_e4m3fn)
+        else:
+            self.pool = torch.empty((num_blocks, 2, 16, Hkv, D), dtype=W.torch_dtype(dtype), device="cuda")
+            W.fill_canary(self.pool, pool_dtype)
         self.scale = float(np.float32(1.0 / np.sqrt(D)))
         self.state = {}
         self.cached = {}
@@ -134,15 +141,23 @@ class Driver:
             k.append(self.rows(STREAM_K, toks, new, self.Hkv))
             v.append(self.rows(STREAM_V, toks, new, self.Hkv))
             allp = np.arange(C + n)
-            kk = W.to_f64(self.rows(STREAM_K, toks, allp, self.Hkv), self.dtype)
-            vv = W.to_f64(self.rows(STREAM_V, toks, allp, self.Hkv), self.dtype)
+            kr, vr = self.rows(STREAM_K, toks, allp, self.Hkv), self.rows(STREAM_V, toks, allp, self.Hkv)
+            if self.fp8:  # what an 8-bit pool holds: the oracle's codes, read back times the scale
+                ks, vs = self.fp8
+                kk = oracle.fp8_decode(oracle.fp8_quantize(kr, self.dtype, ks)) * np.float64(np.float32(ks))
+                vv = oracle.fp8_decode(oracle.fp8_quantize(vr, self.dtype, vs)) * np.float64(np.float32(vs))
+            else:
+                kk, vv = W.to_f64(kr, self.dtype), W.to_f64(vr, self.dtype)
             refs.append(dense_attention(W.to_f64(q[-1], self.dtype), kk, vv, C, self.scale))
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         say(f"[multistep] step {step}: {list(zip(ids, nn))} seq_lens {meta['seq_lens'].tolist()}")
-        out = self.pa.step(self.to_dev(np.concatenate(q)), self.to_dev(np.concatenate(k)),
-                           self.to_dev(np.concatenate(v)), self.pool[:, 0], self.pool[:, 1],
-                           t(meta["slot_mapping"]), t(meta["block_tables"]), t(meta["query_start_loc"]),
-                           t(meta["seq_lens"]), t(meta["context_lens"]), self.scale)
+        args = (self.to_dev(np.concatenate(q)), self.to_dev(np.concatenate(k)), self.to_dev(np.concatenate(v)),
+                self.pool[:, 0], self.pool[:, 1], t(meta["slot_mapping"]), t(meta["block_tables"]),
+                t(meta["query_start_loc"]), t(meta["seq_lens"]), t(meta["context_lens"]))
+        if self.fp8:
+            out = self.pa.step_fp8(*args, self.scale, *self.fp8)
+        else:
+            out = self.pa.step(*args, self.scale)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy().astype(np.float64)
         assert_within(got, np.concatenate(refs), self.dtype, f"step {step}")
@@ -163,3 +178,12 @@ def test_multistep_with_and_without_prefix_caching(pa, dtype, Hq, Hkv, D):
     assert on.cached == {0: 0, 1: 32, 2: 64, 3: 0, 4: 0, 5: 32}
     assert all(c == 0 for c in off.cached.values())
     assert on.mgr.num_free_blocks == off.mgr.num_free_blocks == 96
+
+
+def test_multistep_over_an_8bit_pool(pa):
+    """The same requests over an 8-bit pool: every step's codes are written by
+    the library and read back by later steps (prefix hits included)."""
+    say("[multistep] fp8 pool, bf16 Hq 8 Hkv 2 D 128")
+    on = Driver(pa, True, "bf16", 8, 2, 128, fp8_scales=(0.6, 0.35))
+    assert on.run(requests()) > 0
+    assert on.cached == {0: 0, 1: 32, 2: 64, 3: 0, 4: 0, 5: 32}
