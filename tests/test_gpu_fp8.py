@@ -83,6 +83,8 @@ MIXES = [  # (Hq, Hkv, D, decode contexts, chunks as (cached, new), seed)
     (32, 8, 128, [64, 900, 4100], [(37, 3), (500, 4), (2000, 64)], 2),
     (8, 8, 64, [5, 333], [(200, 40), (0, 16)], 3),
     (16, 2, 64, [77, 1025, 3000], [(1, 2), (400, 33)], 4),
+    (8, 8, 128, [40, 2000], [(300, 300), (0, 40)], 5),  # 1 query head per KV head: 256-token tiles
+    (16, 8, 128, [700], [(900, 200), (64, 9)], 6),  # 2 per KV head: 128-token tiles
 ]
 
 
