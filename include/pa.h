@@ -42,9 +42,17 @@
  *    size) return a pa_status before anything is launched; the text of the
  *    last failure of the calling thread is in pa_last_error(). Launch
  *    failures return PA_ERR_HIP. Device-side contents (ids, lengths, slots)
- *    are not validated: values outside their documented range give
+ *    are not validated by default: values outside their documented range give
  *    unspecified results, but every device access stays inside the tensors
  *    passed in (ids and lengths are clamped, out-of-range slots skipped).
+ *    With PA_VALIDATE=1 in the environment (read at each call), each call
+ *    first copies its metadata to the host, after the work already queued on
+ *    `stream` (so not under graph capture), and returns PA_ERR_CONTENTS,
+ *    launching nothing, unless: query_start_loc[0] = 0, each sequence has at
+ *    least one new token, query_start_loc[S] = T; seq_lens = context_lens +
+ *    new tokens with context_lens >= 0; ceil(seq_len / 16) <= max blocks and
+ *    those table entries lie in [0, num_blocks); every slot is negative or
+ *    below num_blocks * 16, and no two tokens share a slot.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -66,7 +74,8 @@ typedef enum {
   PA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than pa_attention_workspace_size() */
   PA_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed */
   PA_ERR_NO_BLOCKS = 8,   /* KV manager: too few free blocks; nothing changed */
-  PA_ERR_REQUEST = 9      /* KV manager: unknown or duplicate request id, or a token count it does not hold */
+  PA_ERR_REQUEST = 9,     /* KV manager: unknown or duplicate request id, or a token count it does not hold */
+  PA_ERR_CONTENTS = 10    /* PA_VALIDATE=1 only: block ids, lengths, query_start_loc or slots invalid */
 } pa_status;
 
 /* PA_FP8_E4M3: OCP FP8 E4M3 codes (1 byte: sign, 4 exponent bits with bias

@@ -32,6 +32,7 @@ PA_F32, PA_BF16, PA_I32, PA_I64, PA_FP8_E4M3 = 0, 1, 2, 3, 4
 STATUS = {
     0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_DTYPE", 3: "PA_ERR_SHAPE", 4: "PA_ERR_STRIDE",
     5: "PA_ERR_UNSUPPORTED", 6: "PA_ERR_WORKSPACE", 7: "PA_ERR_HIP", 8: "PA_ERR_NO_BLOCKS", 9: "PA_ERR_REQUEST",
+    10: "PA_ERR_CONTENTS",
 }
 EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
            "pa_step_fp8", "pa_attention_workspace_size", "pa_partition_tokens", "pa_status_string", "pa_last_error",

@@ -1,13 +1,15 @@
 // C-ABI entry points of libpa.so: host-side validation of the tensor
 // descriptors, workspace layout, and dispatch to the HIP kernel launchers.
-// Nothing here touches device memory or synchronises the device, so every
-// validation path runs (and is tested) on a machine without a GPU.
+// The descriptor checks touch no device memory and do not synchronise, so
+// they run (and are tested) on a machine without a GPU. Only the opt-in
+// content check (environment PA_VALIDATE=1) copies the metadata to the host.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -454,12 +456,83 @@ extern "C" {
 
 namespace {
 
+// Content checks, only with PA_VALIDATE=1 in the environment (read at each
+// call). They copy the metadata to the host after the work queued on the
+// stream (so a stream under graph capture cannot use them) and apply the
+// rules of a flattened step: query_start_loc starts at 0, grows by at least
+// one token per sequence and ends at T ("Inside vLLM", section "Run forward
+// pass": one super-sequence of all the step's tokens); a sequence's length is
+// its cached context plus its new tokens; its first ceil(length / 16) table
+// entries are pool block ids ("Serving models at scale with vLLM", section
+// "PagedAttention"); each slot is negative (skipped) or inside the pool, and
+// no two tokens share one.
+bool validate_contents() {
+  const char* e = std::getenv("PA_VALIDATE");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+template <class T>
+pa_status to_host(std::vector<T>& h, const T* d, size_t n, hipStream_t s) {
+  h.resize(n);
+  if (n == 0) return ok();
+  PA_TRY(hip_status(hipMemcpyAsync(h.data(), d, n * sizeof(T), hipMemcpyDeviceToHost, s), "PA_VALIDATE copy"));
+  return hip_status(hipStreamSynchronize(s), "PA_VALIDATE sync");
+}
+
+pa_status check_write_contents(const pa::WriteArgs& w, hipStream_t s) {
+  std::vector<int64_t> slots;
+  PA_TRY(to_host(slots, w.slots, size_t(w.T), s));
+  const int64_t nslots = w.NB * pa::kBlockTokens;
+  std::vector<int64_t> used;
+  for (int64_t t = 0; t < w.T; ++t) {
+    if (slots[t] < 0) continue;
+    if (slots[t] >= nslots)
+      return fail(PA_ERR_CONTENTS, "slot_mapping[%lld] = %lld is past the pool (%lld slots)", (long long)t,
+                  (long long)slots[t], (long long)nslots);
+    used.push_back(slots[t]);
+  }
+  std::sort(used.begin(), used.end());
+  const auto dup = std::adjacent_find(used.begin(), used.end());
+  if (dup != used.end()) return fail(PA_ERR_CONTENTS, "slot %lld is written by two tokens", (long long)*dup);
+  return ok();
+}
+
+pa_status check_attention_contents(const pa::AttnArgs& a, hipStream_t s) {
+  std::vector<int32_t> qsl, sl, cl, bt;
+  PA_TRY(to_host(qsl, a.qsl, size_t(a.S + 1), s));
+  PA_TRY(to_host(sl, a.seq_lens, size_t(a.S), s));
+  PA_TRY(to_host(cl, a.ctx_lens, size_t(a.S), s));
+  PA_TRY(to_host(bt, a.block_tables, a.S > 0 ? size_t((a.S - 1) * a.bt_row + a.MB) : 0, s));
+  if (qsl[0] != 0) return fail(PA_ERR_CONTENTS, "query_start_loc[0] = %d, expected 0", qsl[0]);
+  if (qsl[a.S] != a.T)
+    return fail(PA_ERR_CONTENTS, "query_start_loc[S] = %d, expected T = %lld", qsl[a.S], (long long)a.T);
+  for (int64_t i = 0; i < a.S; ++i) {
+    const int64_t n = int64_t(qsl[i + 1]) - qsl[i];
+    if (n < 1) return fail(PA_ERR_CONTENTS, "sequence %lld has %lld new tokens (at least 1)", (long long)i, (long long)n);
+    if (cl[i] < 0 || int64_t(sl[i]) != cl[i] + n)
+      return fail(PA_ERR_CONTENTS, "sequence %lld: seq_len %d != context_len %d + %lld new tokens", (long long)i, sl[i],
+                  cl[i], (long long)n);
+    const int64_t nb = (int64_t(sl[i]) + pa::kBlockTokens - 1) / pa::kBlockTokens;
+    if (nb > a.MB)
+      return fail(PA_ERR_CONTENTS, "sequence %lld needs %lld blocks, block_tables has %lld columns", (long long)i,
+                  (long long)nb, (long long)a.MB);
+    for (int64_t j = 0; j < nb; ++j) {
+      const int32_t id = bt[size_t(i * a.bt_row + j)];
+      if (id < 0 || id >= a.NB)
+        return fail(PA_ERR_CONTENTS, "block_tables[%lld][%lld] = %d is outside the pool (%lld blocks)", (long long)i,
+                    (long long)j, id, (long long)a.NB);
+    }
+  }
+  return ok();
+}
+
 pa_status reshape_and_cache_impl(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
                                  const pa_tensor* value_cache, const pa_tensor* slot_mapping, bool fp8, float k_scale,
                                  float v_scale, pa_stream stream) {
   pa::WriteArgs a{};
   PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, fp8, k_scale, v_scale, &a));
   if (a.T == 0) return ok();
+  if (validate_contents()) PA_TRY(check_write_contents(a, static_cast<hipStream_t>(stream)));
   PA_TRY(hip_status(pa::launch_kv_write(a, static_cast<hipStream_t>(stream)), "kv write launch"));
   return ok();
 }
@@ -471,6 +544,7 @@ pa_status attention_impl(const pa_tensor* out, const pa_tensor* q, const pa_tens
   pa::AttnArgs a{};
   PA_TRY(validate_attention(out, q, key_cache, value_cache, block_tables, query_start_loc, seq_lens, context_lens,
                             scale, fp8, k_scale, v_scale, workspace, workspace_bytes, &a));
+  if (validate_contents()) PA_TRY(check_attention_contents(a, static_cast<hipStream_t>(stream)));
   PA_TRY(run_attention(a, static_cast<hipStream_t>(stream)));
   return ok();
 }
@@ -488,6 +562,10 @@ pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k
   if (w.T != a.T)
     return fail(PA_ERR_SHAPE, "k has %lld tokens, q has %lld", (long long)w.T, (long long)a.T);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (validate_contents()) {
+    if (w.T > 0) PA_TRY(check_write_contents(w, s));
+    PA_TRY(check_attention_contents(a, s));
+  }
   if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
   PA_TRY(run_attention(a, s));
   return ok();
@@ -567,6 +645,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_NO_BLOCKS: return "not enough free KV blocks";
     case PA_ERR_REQUEST: return "unknown request or token count";
+    case PA_ERR_CONTENTS: return "device metadata invalid (PA_VALIDATE)";
   }
   return "unknown status";
 }

@@ -220,8 +220,9 @@ def test_step_checks_token_counts():
 
 
 def test_status_strings():
-    for code in range(8):
-        assert lib.pa_status_string(code)
+    names = [lib.pa_status_string(code) for code in range(11)]  # PA_OK .. PA_ERR_CONTENTS
+    assert all(names) and len(set(names)) == 11 and b"unknown status" not in names
+    assert lib.pa_status_string(11) == b"unknown status"
     assert lib.pa_version() >= 100
 
 
