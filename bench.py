@@ -447,6 +447,29 @@ def prefill_timing_note(head: dict) -> str:
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 
+def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """What a plain device-to-device copy reaches on this GPU, in GB/s (bytes
+    read plus bytes written), best of `reps`: the practical HBM ceiling that
+    the decode's fraction is also quoted against."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / best / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,6 +508,8 @@ def main():
             r = measure(cfg, args.secondary_steps, 1, flush=args.flush, graph=not args.no_graph)
             log(f"[bench] cfg {cfg}: {json.dumps(r)}")
             secondary[r["workload"]] = r
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy: {copy_gbs:.1f} GB/s (read + write of 1 GiB, best of 10)")
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -538,6 +563,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": (dec / HBM_PEAK_GBS) if dec else None,
+            "copy_gbs": copy_gbs,
+            "frac_of_copy": (dec / copy_gbs) if dec else None,
             "traffic": kernel_traffic("decode", head["workload"]),
             "algorithmic_bytes": head.get("decode_kernel_bytes"),
         },
