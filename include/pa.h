@@ -48,11 +48,12 @@
  *    With PA_VALIDATE=1 in the environment (read at each call), each call
  *    first copies its metadata to the host, after the work already queued on
  *    `stream` (so not under graph capture), and returns PA_ERR_CONTENTS,
- *    launching nothing, unless: query_start_loc[0] = 0, each sequence has at
- *    least one new token, query_start_loc[S] = T; seq_lens = context_lens +
- *    new tokens with context_lens >= 0; ceil(seq_len / 16) <= max blocks and
- *    those table entries lie in [0, num_blocks); every slot is negative or
- *    below num_blocks * 16, and no two tokens share a slot.
+ *    launching nothing, unless: query_start_loc[0] = 0, query_start_loc
+ *    never decreases and query_start_loc[S] <= T (a sequence may have no new
+ *    token; rows past query_start_loc[S] are padding); seq_lens =
+ *    context_lens + new tokens with context_lens >= 0; ceil(seq_len / 16) <=
+ *    max blocks and those table entries lie in [0, num_blocks); every slot
+ *    is negative or below num_blocks * 16, and no two tokens share a slot.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -138,6 +139,13 @@ pa_status pa_reshape_and_cache(const pa_tensor* k, const pa_tensor* v, const pa_
  *                  bytes, 256-byte aligned; contents need no initialisation
  *                  and are overwritten. Concurrent calls need separate ones.
  * Supported: D in {64, 128}; Hq % Hkv == 0 and Hq / Hkv <= 16.
+ * Cite: "Inside vLLM", section "Run forward pass", step 3 (one flattened
+ * super-sequence, each sequence masked to its own tokens; the model runner
+ * prepares the block tables and context lengths); "Serving models at scale
+ * with vLLM", section "PagedAttention" (a block table lists a request's
+ * blocks in order) and section "Chunked prefill" (a chunk's tokens attend
+ * the earlier chunks' K/V read back from the cache, and each token only the
+ * tokens before it).
  */
 pa_status pa_attention(const pa_tensor* out, const pa_tensor* q, const pa_tensor* key_cache,
                        const pa_tensor* value_cache, const pa_tensor* block_tables,

@@ -48,6 +48,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr size_t kDecodeMaxLds = 80 * 1024;  // dynamic LDS a decode workgroup may ask for
+constexpr size_t kDecodeRingMaxLds = 128 * 1024;  // the largest ring (8 waves x 2 stages x 8 KB)
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -323,6 +324,58 @@ __device__ inline void attend_block(RawBlock<BF16, D, KV8>& raw, const uint4 (&q
   }
 }
 
+// The waves of each head have left (max, weight sum, unnormalised output)
+// per column in LDS, [wave][m: 16][l: 16][o: ncol * D]; combine those of
+// the same head (waves hl, hl + hw, ...) and store the result: normalised
+// into out for a one-partition sequence, else as the partition's partial.
+template <bool BF16, int D, bool KV8>
+__device__ inline void combine_waves(const AttnArgs& a, const float* smem, int wstride, int hw, int wph, int ncol,
+                                     uint32_t hg, int G, int q0, int nparts, int p) {
+  constexpr int ES = BF16 ? 2 : 4;
+  const int per_head = ncol * (D / 4);
+  for (int idx = threadIdx.x; idx < hw * per_head; idx += kDecodeThreads) {
+    const int hl = idx / per_head, rest = idx - hl * per_head;
+    const int h = rest / (D / 4), d = 4 * (rest - h * (D / 4));  // h: column
+    float m = -INFINITY;
+    for (int ph = 0; ph < wph; ++ph) m = fmaxf(m, smem[(hl + hw * ph) * wstride + h]);
+    float lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ph = 0; ph < wph; ++ph) {
+      const float* wsw = smem + (hl + hw * ph) * wstride;
+      // 0 for a wave that saw no block or no visible key of this column
+      const float sw = m == -INFINITY ? 0.f : fast_exp2(wsw[h] - m);
+      lsum += sw * wsw[16 + h];
+      const float4 x = *reinterpret_cast<const float4*>(wsw + 32 + h * D + d);
+      acc.x += sw * x.x;
+      acc.y += sw * x.y;
+      acc.z += sw * x.z;
+      acc.w += sw * x.w;
+    }
+    if constexpr (KV8) {  // values read back as value(code) * v_scale
+      acc.x *= a.v_scale;
+      acc.y *= a.v_scale;
+      acc.z *= a.v_scale;
+      acc.w *= a.v_scale;
+    }
+    const int64_t hq = int64_t(hg * hw + hl) * G + h % G;
+    const int64_t t = q0 + h / G;  // the column's token
+    if (nparts == 1) {
+      const float inv = 1.f / lsum;
+      char* dst = a.out + t * a.out_st + hq * a.out_sh + d * ES;
+      if constexpr (BF16) {
+        *reinterpret_cast<uint2*>(dst) =
+            make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
+      } else {
+        *reinterpret_cast<float4*>(dst) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      }
+    } else {
+      const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
+      *reinterpret_cast<float4*>(a.ws_o + slot * D + d) = acc;
+      if (d == 0) a.ws_ml[slot] = make_float2(m, lsum);
+    }
+  }
+}
+
 // Workgroup: 8 waves, (sequence s, group of HW KV heads, partition p); grid
 // x = s * (Hkv / HW) + head group, y = p. Wave w serves KV head w % HW and,
 // of the partition's blocks, those with index = w / HW modulo 8 / HW. With
@@ -453,48 +506,280 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     }
   }
   __syncthreads();
-  const int per_head = ncol * (D / 4);
-  for (int idx = threadIdx.x; idx < hw * per_head; idx += kDecodeThreads) {
-    const int hl = idx / per_head, rest = idx - hl * per_head;
-    const int h = rest / (D / 4), d = 4 * (rest - h * (D / 4));  // h: column
-    float m = -INFINITY;
-    for (int ph = 0; ph < wph; ++ph) m = fmaxf(m, smem[(hl + hw * ph) * wstride + h]);
-    float lsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int ph = 0; ph < wph; ++ph) {
-      const float* wsw = smem + (hl + hw * ph) * wstride;
-      // 0 for a wave that saw no block or no visible key of this column
-      const float sw = m == -INFINITY ? 0.f : fast_exp2(wsw[h] - m);
-      lsum += sw * wsw[16 + h];
-      const float4 x = *reinterpret_cast<const float4*>(wsw + 32 + h * D + d);
-      acc.x += sw * x.x;
-      acc.y += sw * x.y;
-      acc.z += sw * x.z;
-      acc.w += sw * x.w;
+  combine_waves<BF16, D, KV8>(a, smem, wstride, hw, wph, ncol, hg, G, q0, nparts, p);
+}
+
+// ------------------------------------------------------- bf16 pool, LDS ring --
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// The memory clobber keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 16 bytes per lane straight into LDS: lane l's bytes land at dst + 16 l (dst
+// is wave-uniform). An offset at or past the resource's size reads zeros.
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t off, lds_char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(dst), 16, off, 0, 0, kStreamPolicy);
+}
+
+// One stage of a wave's ring: one block's K slice of the wave's KV head (16
+// rows of D bf16), then its V slice, in the layouts the fragment reads of
+// the register-staged path use (chunk c of row r at c ^ swz(r)).
+template <int D>
+struct RingStage {
+  static constexpr int ROWB = D * 2;                  // bytes of one row's head slice
+  static constexpr int LPR = ROWB / 16;               // lanes per row in a load (8 or 16)
+  static constexpr int RPI = 64 / LPR;                // rows per load instruction (8 or 4)
+  static constexpr int LPH = kBlockTokens / RPI;      // load instructions per K (or V) slice
+  static constexpr int HALF = kBlockTokens * ROWB;    // bytes of a K (or V) slice
+  static constexpr int BYTES = 2 * HALF;
+  static constexpr int LOADS = 2 * LPH;               // vector-memory operations per block
+  using Sh = DecodeShape<true, D>;
+  __device__ static int k_off(int r, int c) { return Sh::kt_off(r, c); }
+  __device__ static int v_off(int r, int e) { return HALF + Sh::vt_off(r, e); }
+};
+
+// The sweep of one wave over its blocks with an NS-deep ring of LDS stages:
+// a block's K and V go from HBM straight into a stage (no registers hold data
+// in flight), NS blocks are requested ahead, and a stage is refilled as soon
+// as its block has been consumed. dma and rd are two views of the same LDS:
+// loads write through dma, fragment reads go through rd; a stage is never
+// read and loaded at once, and the restrict hint lets the compiler see that
+// (otherwise it waits for every load in flight before each LDS read).
+template <int D, int NS>
+__device__ __attribute__((always_inline)) inline void ring_sweep(
+    const AttnArgs& a, const int32_t* __restrict__ bt, lds_char* __restrict__ dma, const lds_char* __restrict__ rd,
+    int b0, int phase, int wph, int nbw, int L, int lim, int end, uint32_t g, const uint4 (&qv)[D / 32],
+    float qk_scale, f32x4 (&o)[D / 16], float& m_run, float& l_run) {
+  using St = RingStage<D>;
+  constexpr int KC = D / 32, NACC = D / 16;
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
+  const char* kbase = a.kc + int64_t(g) * a.kc_sh;
+  const char* vbase = a.vc + int64_t(g) * a.vc_sh;
+  const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + D * 2);
+  const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + D * 2);
+  // Load i of a slice covers rows RPI i .. RPI i + RPI - 1; lane l fills LDS
+  // chunk slot l % LPR of row RPI i + l / LPR, i.e. it fetches the row's
+  // logical chunk (l % LPR) ^ swz(row).
+  uint32_t koff[St::LPH], voff[St::LPH];
+  int row[St::LPH];
+#pragma unroll
+  for (int i = 0; i < St::LPH; ++i) {
+    row[i] = St::RPI * i + lane / St::LPR;
+    const int cs = lane % St::LPR;
+    koff[i] = static_cast<uint32_t>(row[i] * a.kc_sr + 16 * (cs ^ St::Sh::swzk(row[i])));
+    voff[i] = static_cast<uint32_t>(row[i] * a.vc_sr + 16 * (cs ^ St::Sh::swz(row[i])));
+  }
+  // Block ids of the wave's blocks (at most 128: a partition has at most
+  // 2048 tokens), one per lane in two registers, loaded before the sweep so
+  // that no load inside it makes the compiler wait for the ring (indices
+  // clamped into the table row: entries past the wave's blocks are unused).
+  auto ids_window = [&](int w) {
+    const int64_t j = int64_t(b0) + phase + int64_t(wph) * (64 * w + lane);
+    return bt[j < a.MB ? j : a.MB - 1];
+  };
+  int ids0 = ids_window(0), ids1 = ids_window(1);
+  asm volatile("" ::"v"(ids0), "v"(ids1));  // both have landed before the first request
+  // Request block ib of the wave into stage st. Past the wave's blocks every
+  // lane reads past the resource (zeros, no memory traffic), so each block
+  // issues the same number of loads and the waits below can count them.
+  auto request = [&](int st, int ib) {
+    const int idr = ib < 64 ? ids0 : ids1;
+    const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readlane(idr, ib & 63));
+    const int64_t pid = id < NB ? int64_t(id) : 0;
+    const int blk = b0 + phase + wph * ib;
+    const int rows = ib < nbw ? min(kBlockTokens, L - blk * kBlockTokens) : 0;  // rows of the block inside L
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + pid * a.kc_sb, k_rec);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + pid * a.vc_sb, v_rec);
+    lds_char* dst = dma + st * St::BYTES;
+#pragma unroll
+    for (int i = 0; i < St::LPH; ++i) load_lds16(kr, row[i] < rows ? koff[i] : 0x80000000u, dst + 1024 * i);
+#pragma unroll
+    for (int i = 0; i < St::LPH; ++i)
+      load_lds16(vr, row[i] < rows ? voff[i] : 0x80000000u, dst + St::HALF + 1024 * i);
+  };
+  // Per-lane fragment addresses within a stage: K row n at chunk 4c + kg
+  // (the A operand of k-step c); V^T of tile t through the transposing read
+  // (lane (kg, n) points at V[4kg + n/4][16t + 4(n%4) ..] and receives
+  // V[4kg + e][16t + n], e = 0..3).
+  uint32_t k_rd[KC], v_rd[NACC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) k_rd[c] = static_cast<uint32_t>(St::k_off(n, 4 * c + kg));
+#pragma unroll
+  for (int t = 0; t < NACC; ++t) v_rd[t] = static_cast<uint32_t>(St::v_off(4 * kg + (n >> 2), 16 * t + 4 * (n & 3)));
+
+  // Consume the block in stage st: scores S^T[token 4kg + r][column n], online
+  // softmax, O^T += V^T P^T. Rows past the sequence end hold zeros.
+  auto consume = [&](int st, int blk) {
+    const lds_char* sb = rd + st * St::BYTES;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const u32x4 kc = *reinterpret_cast<lds_cu32x4*>(sb + k_rd[c]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc), __builtin_bit_cast(bf16x8, qv[c]),
+                                                     acc, 0, 0, 0);
     }
-    if constexpr (KV8) {  // values read back as value(code) * v_scale
-      acc.x *= a.v_scale;
-      acc.y *= a.v_scale;
-      acc.z *= a.v_scale;
-      acc.w *= a.v_scale;
+    float sc[4];
+    const int tok0 = blk * kBlockTokens + 4 * kg;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim) ? acc[r] * qk_scale : -INFINITY;
+    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    // a column with no visible key yet keeps maximum -inf and weights 0
+    if (__any(mloc > m_run + kRescaleThreshold)) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = m_new == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < NACC; ++t) o[t] *= alpha;
+      m_run = m_new;
     }
-    const int64_t hq = int64_t(hg * hw + hl) * G + h % G;
-    const int64_t t = q0 + h / G;  // the column's token
-    if (nparts == 1) {
-      const float inv = 1.f / lsum;
-      char* dst = a.out + t * a.out_st + hq * a.out_sh + d * ES;
-      if constexpr (BF16) {
-        *reinterpret_cast<uint2*>(dst) =
-            make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
-      } else {
-        *reinterpret_cast<float4*>(dst) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    float pr[4];
+    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = fast_exp2(sc[r] - m_ref);
+      l_run += pr[r];
+    }
+    const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])));
+#pragma unroll
+    for (int t = 0; t < NACC; ++t) {
+      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<lds_char*>(sb) + v_rd[t]));
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[t], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int j = 0; j < NS; ++j) request(j, j);
+  for (int i = 0; i < nbw; i += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int ib = i + j;
+      if (ib < nbw) {
+        // stage j has landed once at most the NS - 1 later blocks' loads are in flight
+        wait_vmem<(NS - 1) * St::LOADS>();
+        consume(j, b0 + phase + wph * ib);
+        // the stage's fragment reads are done before it is refilled
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        request(j, ib + NS);
       }
-    } else {
-      const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
-      *reinterpret_cast<float4*>(a.ws_o + slot * D + d) = acc;
-      if (d == 0) a.ws_ml[slot] = make_float2(m, lsum);
     }
   }
+  // No load may still be writing LDS when the stages are reused or freed.
+  wait_vmem<0>();
+}
+
+// bf16 pools: like decode_kernel (same grid and workgroups, same results up
+// to the order of fp32 additions), but each wave streams its blocks through an
+// NS-stage LDS ring. With one wave per KV head (8 heads per workgroup) the
+// waves store their results themselves and never wait for each other.
+template <int D, int NS>
+__global__ __launch_bounds__(kDecodeThreads) void decode_ring_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
+                                                                     int hw) {
+  using St = RingStage<D>;
+  constexpr int KC = D / 32, NACC = D / 16;
+  extern __shared__ uint4 lds_dyn[];
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wph = kDecodeWaves / hw;  // waves per KV head
+  const uint32_t n_hg = static_cast<uint32_t>(a.Hkv / hw);
+  const uint32_t s = blockIdx.x / n_hg, hg = blockIdx.x - s * n_hg;
+  const uint32_t g = hg * hw + wave % hw;
+  const int phase = wave / hw;
+  const int p = blockIdx.y;
+  const int PT = static_cast<int>(a.part_tokens);
+  const int b0 = p * (PT / kBlockTokens);
+  const int32_t* bt = bt_all + int64_t(s) * a.bt_row;
+  const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
+  const int G = static_cast<int>(a.Hq / a.Hkv);
+  const int nq = q1 - q0;
+  if (!decode_path(nq, G) || q0 < 0 || q1 > a.T) return;  // whole workgroup
+  const int L = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
+  const int start = p * PT;
+  if (start >= L) return;  // whole workgroup
+  const int end = min(start + PT, L);
+  const int nparts = (L + PT - 1) / PT;
+  const int ncol = nq * G;
+  const int C = min(max(a.ctx_lens[s], 0), L);
+  const int lim = min(end, C + n / G + 1);
+  const float qk_scale = a.scale * kLog2e;
+  const int nblk = (end - start + kBlockTokens - 1) / kBlockTokens;
+  const int nbw = nblk > phase ? (nblk - phase + wph - 1) / wph : 0;
+
+  uint4 qv[KC];
+  {
+    const int qi = n < ncol ? n / G : 0, qh = n < ncol ? n % G : 0;
+    const char* qrow = a.q + int64_t(q0 + qi) * a.q_st + int64_t(g * G + qh) * a.q_sh + 16 * kg;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qv[c] = n < ncol ? *reinterpret_cast<const uint4*>(qrow + 64 * c) : make_uint4(0, 0, 0, 0);
+  }
+  f32x4 o[NACC];
+#pragma unroll
+  for (int t = 0; t < NACC; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  {
+    // The load view is offset by an opaque zero so that the two views are
+    // distinct values (identical arguments would defeat the restrict hint).
+    uint32_t zero = 0;
+    asm volatile("" : "+s"(zero));
+    const uint32_t base = static_cast<uint32_t>(wave) * NS * St::BYTES;
+    ring_sweep<D, NS>(a, bt, (lds_char*)lds_dyn + base + zero,
+                      (const lds_char*)lds_dyn + base, b0, phase, wph, nbw, L, lim, end, g, qv,
+                      qk_scale, o, m_run, l_run);
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (wph == 1) {
+    // this wave alone holds its head's result: lane (kg, n) has column n,
+    // d = 16t + 4kg .. + 3
+    if (n < ncol) {
+      const int64_t hq = int64_t(g) * G + n % G;
+      const int64_t t = q0 + n / G;
+      if (nparts == 1) {
+        const float inv = 1.f / l_tot;
+        char* dst = a.out + t * a.out_st + hq * a.out_sh + 8 * kg;
+#pragma unroll
+        for (int u = 0; u < NACC; ++u)
+          *reinterpret_cast<uint2*>(dst + 32 * u) =
+              make_uint2(pack_bf16(o[u][0] * inv, o[u][1] * inv), pack_bf16(o[u][2] * inv, o[u][3] * inv));
+      } else {
+        const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
+#pragma unroll
+        for (int u = 0; u < NACC; ++u)
+          *reinterpret_cast<float4*>(a.ws_o + slot * D + 16 * u + 4 * kg) = make_float4(o[u][0], o[u][1], o[u][2], o[u][3]);
+        if (kg == 0) a.ws_ml[slot] = make_float2(m_run, l_tot);
+      }
+    }
+    return;
+  }
+  // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: ncol * D]
+  __syncthreads();  // every wave's ring is drained
+  float* smem = reinterpret_cast<float*>(lds_dyn);
+  const int wstride = 32 + ncol * D;
+  float* ws = smem + wave * wstride;
+  if (kg == 0) {
+    ws[n] = m_run;
+    ws[16 + n] = l_tot;
+  }
+  if (n < ncol) {
+#pragma unroll
+    for (int u = 0; u < NACC; ++u)
+      *reinterpret_cast<float4*>(ws + 32 + n * D + 16 * u + 4 * kg) = make_float4(o[u][0], o[u][1], o[u][2], o[u][3]);
+  }
+  __syncthreads();
+  combine_waves<true, D, false>(a, smem, wstride, hw, wph, ncol, hg, G, q0, nparts, p);
 }
 
 // Combine the partitions of multi-partition sequences of the decode kernel:
@@ -559,8 +844,23 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(AttnArgs a) {
   }
 }
 
-template <bool BF16, int D, int NPF, bool KV8>
-hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream, bool bf16) {
+  if (a.max_parts <= 1) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((a.S * a.Hq + kWaves - 1) / kWaves));
+  ProfileScope ps(kReduce, stream);
+  if (a.D == 64) {
+    if (bf16) hipLaunchKernelGGL((reduce_kernel<true, 64>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((reduce_kernel<false, 64>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((reduce_kernel<true, 128>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((reduce_kernel<false, 128>), grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+// fp32 and 8-bit pools: the register-staged kernel.
+template <bool BF16, int D, bool KV8>
+hipError_t launch_staged(const AttnArgs& a, hipStream_t stream) {
   using Sh = DecodeShape<BF16, D>;
   const int hw = decode_heads_per_workgroup(a.Hkv);
   const size_t merge = sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D);  // up to 16 columns
@@ -569,52 +869,66 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
   // 16 query heads per KV head at D = 128 need 65 KB for the merge.
   static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, NPF, KV8>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, 1, KV8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeMaxLds));
   if (attr != hipSuccess) return attr;
   if (lds > kDecodeMaxLds) return hipErrorInvalidValue;
   {
     ProfileScope ps(kDecode, stream);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, NPF, KV8>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
+    hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV8>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
                        hw);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_parts <= 1) return e;
-  const int64_t rblocks = (a.S * a.Hq + kWaves - 1) / kWaves;
-  {
-    ProfileScope ps(kReduce, stream);
-    hipLaunchKernelGGL((reduce_kernel<BF16, D>), dim3(static_cast<unsigned>(rblocks)), dim3(kThreads), 0, stream,
-                       a);
-  }
-  return hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(a, stream, BF16);
 }
 
-int prefetch_depth() {
+// bf16 pools: the LDS-ring kernel with NS stages per wave.
+template <int D, int NS>
+hipError_t launch_ring(const AttnArgs& a, hipStream_t stream) {
+  using St = RingStage<D>;
+  const int hw = decode_heads_per_workgroup(a.Hkv);
+  const size_t ring = size_t(kDecodeWaves) * NS * St::BYTES;
+  const size_t merge = hw < kDecodeWaves ? sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D) : 0;
+  const size_t lds = ring > merge ? ring : merge;
+  static_assert(size_t(kDecodeWaves) * NS * St::BYTES <= kDecodeRingMaxLds, "ring exceeds the LDS of a CU");
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<D, NS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeRingMaxLds));
+  if (attr != hipSuccess) return attr;
+  if (lds > kDecodeRingMaxLds) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
+  {
+    ProfileScope ps(kDecode, stream);
+    hipLaunchKernelGGL((decode_ring_kernel<D, NS>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables, hw);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(a, stream, true);
+}
+
+// Stages per wave of the bf16 ring. PA_DECODE_RING=<n> forces n (for timing).
+int ring_stages(const AttnArgs& a) {
   static const int forced = [] {
-    const char* e = std::getenv("PA_DECODE_PREFETCH");
+    const char* e = std::getenv("PA_DECODE_RING");
     return e ? std::atoi(e) : 0;
   }();
-  return (forced >= 1 && forced <= 3) ? forced : 1;
-}
-
-template <bool BF16, int D>
-hipError_t launch_depth(const AttnArgs& a, hipStream_t stream) {
-  if constexpr (BF16) {
-    if (a.kv8) return launch_typed<true, D, 1, true>(a, stream);
-  }
-  switch (prefetch_depth()) {
-    case 2: return launch_typed<BF16, D, 2, false>(a, stream);
-    case 3: return launch_typed<BF16, D, 3, false>(a, stream);
-    default: return launch_typed<BF16, D, 1, false>(a, stream);
-  }
+  if (forced == 1 || forced == 2 || (forced == 4 && a.D == 64)) return forced;
+  return 1;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
-  const bool bf16 = a.elem == Elem::BF16;
-  if (a.D == 64) return bf16 ? launch_depth<true, 64>(a, stream) : launch_depth<false, 64>(a, stream);
-  return bf16 ? launch_depth<true, 128>(a, stream) : launch_depth<false, 128>(a, stream);
+  if (a.elem != Elem::BF16)
+    return a.D == 64 ? launch_staged<false, 64, false>(a, stream) : launch_staged<false, 128, false>(a, stream);
+  if (a.kv8) return a.D == 64 ? launch_staged<true, 64, true>(a, stream) : launch_staged<true, 128, true>(a, stream);
+  const int ns = ring_stages(a);
+  if (a.D == 64) {
+    if (ns == 4) return launch_ring<64, 4>(a, stream);
+    return ns == 1 ? launch_ring<64, 1>(a, stream) : launch_ring<64, 2>(a, stream);
+  }
+  return ns == 1 ? launch_ring<128, 1>(a, stream) : launch_ring<128, 2>(a, stream);
 }
 
 }  // namespace pa

@@ -415,7 +415,7 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
     const char* e = std::getenv("PA_PARTITION_TOKENS");
     if (!e) return int64_t(0);
     long long v = std::atoll(e);
-    return (v >= kBlockTokens && v % kBlockTokens == 0) ? int64_t(v) : int64_t(0);
+    return (v >= kBlockTokens && v <= kMaxPartitionTokens && v % kBlockTokens == 0) ? int64_t(v) : int64_t(0);
   }();
   if (forced) return forced;
   // A partition is one decode workgroup's share of a sequence: 8 waves over
@@ -425,7 +425,7 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
   constexpr int64_t kMinDecodeWorkgroups = 512;
   const int64_t groups = S * (Hkv / decode_heads_per_workgroup(Hkv));
   const int64_t max_len = MB * kBlockTokens;
-  for (int64_t pt : {2048, 1024, 512, 256, 128, 64}) {
+  for (int64_t pt : {kMaxPartitionTokens, int64_t(1024), int64_t(512), int64_t(256), int64_t(128), int64_t(64)}) {
     const int64_t parts = (max_len + pt - 1) / pt;
     if (groups * parts >= kMinDecodeWorkgroups) return pt;
   }
@@ -450,19 +450,16 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
 
 }  // namespace pa
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
 // Content checks, only with PA_VALIDATE=1 in the environment (read at each
 // call). They copy the metadata to the host after the work queued on the
 // stream (so a stream under graph capture cannot use them) and apply the
-// rules of a flattened step: query_start_loc starts at 0, grows by at least
-// one token per sequence and ends at T ("Inside vLLM", section "Run forward
-// pass": one super-sequence of all the step's tokens); a sequence's length is
-// its cached context plus its new tokens; its first ceil(length / 16) table
+// rules of a flattened step: query_start_loc starts at 0, never decreases and
+// ends at or before T ("Inside vLLM", section "Run forward pass": one
+// super-sequence of all the step's tokens; rows past query_start_loc[S] are
+// padding, as are sequences with no new token); a sequence's length is its
+// cached context plus its new tokens; its first ceil(length / 16) table
 // entries are pool block ids ("Serving models at scale with vLLM", section
 // "PagedAttention"); each slot is negative (skipped) or inside the pool, and
 // no two tokens share one.
@@ -504,11 +501,13 @@ pa_status check_attention_contents(const pa::AttnArgs& a, hipStream_t s) {
   PA_TRY(to_host(cl, a.ctx_lens, size_t(a.S), s));
   PA_TRY(to_host(bt, a.block_tables, a.S > 0 ? size_t((a.S - 1) * a.bt_row + a.MB) : 0, s));
   if (qsl[0] != 0) return fail(PA_ERR_CONTENTS, "query_start_loc[0] = %d, expected 0", qsl[0]);
-  if (qsl[a.S] != a.T)
-    return fail(PA_ERR_CONTENTS, "query_start_loc[S] = %d, expected T = %lld", qsl[a.S], (long long)a.T);
+  if (qsl[a.S] > a.T)
+    return fail(PA_ERR_CONTENTS, "query_start_loc[S] = %d is past T = %lld", qsl[a.S], (long long)a.T);
   for (int64_t i = 0; i < a.S; ++i) {
     const int64_t n = int64_t(qsl[i + 1]) - qsl[i];
-    if (n < 1) return fail(PA_ERR_CONTENTS, "sequence %lld has %lld new tokens (at least 1)", (long long)i, (long long)n);
+    if (n < 0)
+      return fail(PA_ERR_CONTENTS, "query_start_loc decreases at sequence %lld (%d -> %d)", (long long)i, qsl[i],
+                  qsl[i + 1]);
     if (cl[i] < 0 || int64_t(sl[i]) != cl[i] + n)
       return fail(PA_ERR_CONTENTS, "sequence %lld: seq_len %d != context_len %d + %lld new tokens", (long long)i, sl[i],
                   cl[i], (long long)n);

@@ -9,7 +9,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-pa = pytest.importorskip("pagedattention_block_paged_amd")
+# A missing libpa.so is a failure here, not a skip: the import raises.
+import pagedattention_block_paged_amd as pa  # noqa: E402
 from pagedattention_block_paged_amd import Tensor, lib  # noqa: E402
 
 PA_OK, PA_ERR_NULL, PA_ERR_DTYPE, PA_ERR_SHAPE, PA_ERR_STRIDE, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE = range(7)

@@ -98,3 +98,56 @@ def test_unchecked_without_the_variable(pa, wl, monkeypatch):
     monkeypatch.delenv("PA_VALIDATE", raising=False)
     _, err = run_step(pa, wl, slots=bad_cases(wl)["slot past the pool"]["slots"])
     assert err is None
+
+
+def test_zero_query_sequence_and_padding_rows_pass(pa, wl, monkeypatch):
+    """A sequence with no new token (seq_len = context_len) and padding rows
+    past query_start_loc[S] (slot -1) are valid: the checked call accepts them
+    and gives the unchecked call's output bit for bit; padding rows of out and
+    the pool are untouched."""
+    print("[validate] zero-query sequence + padding rows", flush=True)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    keep = [0, 2, 3]  # sequence 1 contributes no row
+    pad = 2
+    q = W.q_device(wl, "cuda")
+    k, v = W.new_kv_device(wl, "cuda")
+    q = torch.cat([q[keep], q[:pad]]).contiguous()
+    k = torch.cat([k[keep], k[:pad]]).contiguous()
+    v = torch.cat([v[keep], v[:pad]]).contiguous()
+    slots = np.concatenate([wl.slot_mapping[keep], np.full(pad, -1, np.int64)])
+    qsl = np.array([0, 1, 1, 2, 3], np.int32)
+    sl = wl.seq_lens.copy()
+    sl[1] = wl.context_lens[1]
+    outs = []
+    for checked in (False, True):
+        if checked:
+            monkeypatch.setenv("PA_VALIDATE", "1")
+        else:
+            monkeypatch.delenv("PA_VALIDATE", raising=False)
+        pool = W.pool_device(wl, "cuda")
+        before = pool.clone()
+        out = torch.full_like(q, 7.0)
+        pa.step(q, k, v, pool[:, 0], pool[:, 1], t(slots), t(wl.block_tables), t(qsl), t(sl), t(wl.context_lens),
+                wl.scale, out=out)
+        torch.cuda.synchronize()
+        s1 = int(wl.slot_mapping[1])  # sequence 1's would-be slot stays unwritten
+        assert torch.equal(pool[s1 // 16, :, s1 % 16].view(torch.int16), before[s1 // 16, :, s1 % 16].view(torch.int16))
+        assert bool((out[3:] == 7.0).all()), "padding rows of out were written"
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
+def test_decreasing_query_start_loc_is_rejected(pa, wl, monkeypatch):
+    """query_start_loc must not decrease (the kernels treat such a sequence as empty)."""
+    print("[validate] decreasing query_start_loc", flush=True)
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = W.q_device(wl, "cuda")
+    k, v = W.new_kv_device(wl, "cuda")
+    pool = W.pool_device(wl, "cuda")
+    qsl = np.array([0, 1, 0, 3, 4], np.int32)
+    with pytest.raises(pa.PAError) as e:
+        pa.step(q, k, v, pool[:, 0], pool[:, 1], t(wl.slot_mapping), t(wl.block_tables), t(qsl), t(wl.seq_lens),
+                t(wl.context_lens), wl.scale)
+    torch.cuda.synchronize()
+    assert e.value.status == PA_ERR_CONTENTS and "decreases" in str(e.value)

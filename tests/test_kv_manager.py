@@ -14,7 +14,8 @@ import pytest
 
 from oracle.block_model import BlockModel, NoBlocks
 
-kvm = pytest.importorskip("pagedattention_block_paged_amd.kv_manager")
+# A missing libpa.so is a failure here, not a skip: the import raises.
+from pagedattention_block_paged_amd import kv_manager as kvm  # noqa: E402
 KVCacheManager = kvm.KVCacheManager
 
 
