@@ -40,20 +40,84 @@ def raw_bytes(x: torch.Tensor) -> np.ndarray:
     return x.cpu().numpy().reshape(-1).view(np.uint8)
 
 
-def sample_seqs(wl, k: int, seed: int = 0):
-    """A sample of sequences that always holds the longest and shortest of each kind."""
-    rs = np.random.default_rng(seed)
-    pick = set()
-    dec = np.nonzero(wl.decode_mask())[0]
-    pre = np.nonzero(~wl.decode_mask())[0]
-    for group in (dec, pre):
-        if group.size:
-            L = wl.seq_lens[group]
-            pick.update([int(group[np.argmax(L)]), int(group[np.argmin(L)])])
-    rest = np.setdiff1d(np.arange(wl.num_seqs), sorted(pick))
-    extra = rs.choice(rest, size=min(k, rest.size), replace=False) if rest.size else []
-    return sorted(pick.union(int(x) for x in extra))
-
-
 def rows_of(wl, seqs):
     return np.concatenate([np.arange(wl.query_start_loc[s], wl.query_start_loc[s + 1]) for s in seqs])
+
+
+def host_inputs(wl, device="cuda"):
+    """Host copies (numpy; bf16 as uint16 bits, fp8 as uint8 codes) of a
+    workload's pool before the KV write, k, v and q, made by the torch twin of
+    the seeded generator on the device (the same bits as the numpy twin,
+    which tests/test_workloads.py checks) -- the generator, not the library."""
+    def h(t):
+        t = t.cpu()
+        if t.dtype == torch.float32:
+            return t.numpy()
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).numpy()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    k, v = W.new_kv_device(wl, device)
+    return h(W.pool_device(wl, device)), h(k), h(v), h(W.q_device(wl, device))
+
+
+def seq_batches(wl, seqs, max_bytes=4e9):
+    """Consecutive groups of `seqs` whose K/V (each sequence's own blocks) stay under max_bytes."""
+    per = -(-wl.seq_lens[seqs].astype(np.int64) // 16) * wl.block_bytes
+    out, cur, acc = [], [], 0
+    for s, b in zip(seqs, per):
+        if cur and acc + b > max_bytes:
+            out.append(cur)
+            cur, acc = [], 0
+        cur.append(int(s))
+        acc += int(b)
+    if cur:
+        out.append(cur)
+    return out
+
+
+class ErrorTally:
+    """Error statistics accumulated over batches of output rows (one row =
+    one token and query head): max abs, mean abs, and the largest per-row
+    max|err| / rms(reference row)."""
+
+    def __init__(self):
+        self.max_abs, self.sum_abs, self.n, self.rel, self.finite, self.rows = 0.0, 0.0, 0, 0.0, True, 0
+
+    def add(self, got, ref):
+        got = np.asarray(got, np.float64)
+        ref = np.asarray(ref, np.float64)
+        assert got.shape == ref.shape, (got.shape, ref.shape)
+        if ref.size == 0:
+            return
+        err = np.abs(got - ref)
+        self.finite &= bool(np.isfinite(got).all())
+        self.max_abs = max(self.max_abs, float(err.max()))
+        self.sum_abs += float(err.sum())
+        self.n += err.size
+        D = ref.shape[-1]
+        row_err = err.reshape(-1, D).max(axis=1)
+        row_rms = np.sqrt(np.mean(ref.reshape(-1, D) ** 2, axis=1))
+        self.rel = max(self.rel, float(np.nanmax(row_err / np.maximum(row_rms, 1e-30))))
+        self.rows += row_err.size
+
+    def summary(self):
+        return {"max_abs": self.max_abs, "mean_abs": self.sum_abs / max(self.n, 1), "rel": self.rel,
+                "finite": self.finite, "rows": self.rows}
+
+
+def oracle_every_row(wl, out, run, say=print, max_bytes=4e9):
+    """Compare every output row of `out` (the device output of workload wl)
+    with the oracle, sequence batch by sequence batch (each batch a compact
+    sub-workload, so the host pool stays a few GB). `run(sub, pool)` runs the
+    oracle on a sub-workload and its host pool. Returns the ErrorTally."""
+    tally = ErrorTally()
+    batches = seq_batches(wl, np.arange(wl.num_seqs), max_bytes)
+    for i, seqs in enumerate(batches):
+        sub = W.sub_workload(wl, seqs)
+        pool, _, _, _ = host_inputs(sub)
+        ref, _ = run(sub, pool)
+        got = to_f64(out[torch.from_numpy(rows_of(wl, seqs)).to(out.device)])
+        tally.add(got, ref)
+        say(f"  batch {i + 1}/{len(batches)}: {len(seqs)} sequences, {tally.rows} rows so far")
+    return tally

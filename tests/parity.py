@@ -8,10 +8,13 @@ Bounds as required for this path:
 The absolute bounds alone are blind at long contexts, where outputs shrink like
 sqrt(e / L) (about 0.009 at 32k keys): an all-zero output would pass the mean
 bound. So bf16 results must also satisfy, for every output row (one token, one
-head: D values), max|err| <= REL_BF16 * rms(ref row). bf16 output rounding alone
-contributes at most 2^-9 * max|ref row| / rms(ref row): about 0.01 on the
-spikiest rows seen (max/rms near 5, short contexts), so the bound leaves 3x
-headroom for fp32 accumulation order and bf16 softmax weights.
+head: D values), max|err| <= REL_BF16 * rms(ref row). The kernels round three
+things to bf16 -- the prefill's pre-scaled Q, the softmax weights before P.V
+and the output -- each by at most 2^-9 relative, and on the spikiest rows
+(max/rms near 5) they add to about 0.03: the worst rows of the full-size
+workloads, every row compared, reach 0.031-0.033. REL_BF16 = 0.04 keeps that
+margin while the mildest planted mistake (the last 512-key partition of a
+32k context dropped) gives 0.61.
 tests/test_tolerance_bites.py shows every planted mistake fails these rules.
 """
 from __future__ import annotations
@@ -21,7 +24,7 @@ import numpy as np
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 2e-2
 BF16_MEAN_ABS = 1e-2
-REL_BF16 = 3e-2
+REL_BF16 = 4e-2
 
 
 def errors(out: np.ndarray, ref: np.ndarray) -> dict:
@@ -64,3 +67,17 @@ def bf16_round_f64(x: np.ndarray) -> np.ndarray:
     from workloads.rng import bf16_bits_to_f32, f32_to_bf16_bits
 
     return bf16_bits_to_f32(f32_to_bf16_bits(np.asarray(x, np.float64).astype(np.float32))).astype(np.float64)
+
+
+def within_summary(e: dict, dtype: str) -> bool:
+    """The bounds above applied to accumulated statistics (tests/gpu_util.py ErrorTally)."""
+    if not e["finite"]:
+        return False
+    if dtype == "f32":
+        return e["max_abs"] <= F32_MAX_ABS
+    return e["max_abs"] <= BF16_MAX_ABS and e["mean_abs"] <= BF16_MEAN_ABS and e["rel"] <= REL_BF16
+
+
+def assert_summary(e: dict, dtype: str, what: str = ""):
+    assert within_summary(e, dtype), f"{what}: {e}"
+    return e

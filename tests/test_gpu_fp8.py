@@ -7,7 +7,7 @@
 - Attention: random mixes of decodes, short chunks (attended by the decode
   kernel) and long chunks (the prefill path) at head sizes 64 and 128 and
   1, 4 and 8 query heads per KV head, and the Llama-3-70B 32k decode batch and
-  the Llama-3-8B mixed step at full size (sampled sequences), against the
+  the Llama-3-8B mixed step at full size (every output row), against the
   oracle on the same codes, to the bf16 bounds: the codes widen to bf16 and
   fp32 exactly, so the pool format adds no error of its own.
 """
@@ -17,8 +17,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import sample_seqs, to_f64
-from parity import assert_within
+from gpu_util import host_inputs, oracle_every_row, to_f64
+from parity import assert_summary, assert_within
 
 pytestmark = pytest.mark.gpu
 
@@ -113,13 +113,46 @@ def run_fp8_step(pa, wl, rows=None):
     return to_f64(out)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg", [4, 3])
-def test_fp8_full_size_sampled(pa, cfg):
+def test_fp8_full_size_every_row(pa, cfg):
+    """The 70B 32k decode and the 8B mixed step over an 8-bit pool at full
+    size: every output row against the oracle on the same codes."""
     base = W.config_workload(cfg, hbm_bytes=torch.cuda.get_device_properties(0).total_memory // 2)
     wl = W.with_fp8_pool(base)
     say(f"[fp8 cfg {cfg}] {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")
-    seqs = sample_seqs(wl, 4)
-    rows = np.concatenate([np.arange(wl.query_start_loc[s], wl.query_start_loc[s + 1]) for s in seqs])
-    out = run_fp8_step(pa, wl, rows)
-    ref, _ = oracle.run_workload(W.sub_workload(wl, seqs))
-    assert_within(out, ref, "bf16", wl.name)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = W.q_device(wl, "cuda")
+    k, v = W.new_kv_device(wl, "cuda")
+    pool = W.pool_device(wl, "cuda")
+    out = pa.step_fp8(q, k, v, pool[:, 0], pool[:, 1], t(wl.slot_mapping), t(wl.block_tables),
+                      t(wl.query_start_loc), t(wl.seq_lens), t(wl.context_lens), wl.scale, wl.k_scale, wl.v_scale)
+    torch.cuda.synchronize()
+    del q, k, v, pool
+    e = oracle_every_row(wl, out, lambda sub, hp: oracle.run_workload(sub, pool=hp), say=say).summary()
+    say(f"[fp8 cfg {cfg}] {e}")
+    assert e["rows"] == wl.num_tokens * wl.num_q_heads
+    assert_summary(e, "bf16", wl.name)
+
+
+def test_fp8_heavier_tailed_context_within_absolute_bounds(pa):
+    """The 8B mixed step's 8 prefill chunks plus 64 of its decodes over an
+    8-bit pool whose cached codes are uniform over magnitudes 1/16 .. 3.75
+    (scales 0.5 and 0.25): spikier softmax rows than N(0, 1) gives. The bf16
+    rounding of the softmax weights before P.V is the prefill's largest error
+    term there, so this case tracks its margin against the stated absolute
+    bounds (max abs 2e-2, mean abs 1e-2); the per-row bound is reported."""
+    base = W.config_workload(3)
+    seqs = list(range(0, 4096, 64)) + list(range(4096, 4104))
+    wl = W.with_fp8_pool(W.sub_workload(base, seqs), 0.5, 0.25, codes="band")
+    say(f"[fp8 band] {wl.name}: S={wl.num_seqs} T={wl.num_tokens}")
+    out = run_fp8_step(pa, wl)
+    pool, _, _, _ = host_inputs(wl)
+    ref, _ = oracle.run_workload(wl, pool=pool)
+    err = np.abs(out - ref)
+    rms = np.sqrt(np.mean(ref.reshape(-1, ref.shape[-1]) ** 2, axis=1))
+    rel = float((err.reshape(-1, ref.shape[-1]).max(axis=1) / rms).max())
+    say(f"[fp8 band] max abs {err.max():.4g} (bound 2e-2), mean abs {err.mean():.4g} (bound 1e-2), "
+        f"per-row max / rms {rel:.4g}")
+    assert np.isfinite(out).all()
+    assert err.max() <= 2e-2 and err.mean() <= 1e-2

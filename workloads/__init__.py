@@ -65,6 +65,9 @@ class Workload:
     kv_dtype: str = ""
     k_scale: float = 1.0
     v_scale: float = 1.0
+    # 8-bit pool contents: "normal" (codes shaped like N(0, 1)) or "band"
+    # (uniform over the magnitudes 1/16 .. 3.75, heavier-tailed)
+    fp8_codes: str = "normal"
 
     @property
     def pool_dtype(self) -> str:
@@ -290,6 +293,8 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
 
 # --- values -------------------------------------------------------------------
 def _table_np(dtype: str) -> np.ndarray:
+    if dtype == "fp8band":
+        return _rng.FP8_CODES_BAND
     if dtype == "fp8":
         return _rng.FP8_CODES
     return _rng.NORMAL_F32 if dtype == "f32" else _rng.NORMAL_BF16
@@ -394,6 +399,11 @@ def prior_blocks(wl: Workload):
     return cat(phys), cat(ident), cat(first), cat(limit)
 
 
+def _context_table(wl: Workload) -> str:
+    """The value table of a workload's cached context."""
+    return "fp8band" if wl.pool_dtype == "fp8" and wl.fp8_codes == "band" else wl.pool_dtype
+
+
 def pool_host(wl: Workload) -> np.ndarray:
     """Host pool [NB, 2, 16, Hkv, D] before the KV write: cached rows placed, canaries elsewhere."""
     Hkv, D, pd = wl.num_kv_heads, wl.head_size, wl.pool_dtype
@@ -407,7 +417,7 @@ def pool_host(wl: Workload) -> np.ndarray:
     idn = np.repeat(ident, BLOCK_SIZE)
     valid = (pos < np.repeat(limit, BLOCK_SIZE)).reshape(-1, BLOCK_SIZE)
     for kv, stream in ((0, STREAM_K), (1, STREAM_V)):
-        vals = _rows_np(_rng.stream_key(wl.seed, stream), idn, pos, Hkv * D, pd)
+        vals = _rows_np(_rng.stream_key(wl.seed, stream), idn, pos, Hkv * D, _context_table(wl))
         vals = vals.reshape(-1, BLOCK_SIZE, Hkv, D)
         vals[~valid] = canary_np(pd)
         pool[phys, kv] = vals
@@ -476,6 +486,8 @@ def with_block_tables(wl: Workload, tables, num_blocks: int, canary_block: int) 
 def _table_torch(dtype: str, device):
     import torch
 
+    if dtype == "fp8band":
+        return torch.from_numpy(_rng.FP8_CODES_BAND.copy()).to(device)
     if dtype == "fp8":
         return torch.from_numpy(_rng.FP8_CODES.copy()).to(device)
     if dtype == "f32":
@@ -539,7 +551,7 @@ def pool_device(wl: Workload, device, *, blocks_per_chunk: int = 8192):
     can = canary_torch(pd, device)
     fill_canary(pool, pd)
     phys, ident, first, limit = prior_blocks(wl)
-    table = _table_torch(pd, device)
+    table = _table_torch(_context_table(wl), device)
     keys = (_rng.stream_key(wl.seed, STREAM_K), _rng.stream_key(wl.seed, STREAM_V))
     r = torch.arange(BLOCK_SIZE, device=device, dtype=torch.int64)
     for a in range(0, phys.size, blocks_per_chunk):
@@ -595,9 +607,12 @@ def token_rows(seed: int, stream: int, idents, positions, heads: int, head_size:
     return rows.reshape(-1, heads, head_size)
 
 
-def with_fp8_pool(wl: Workload, k_scale: float = 1.0, v_scale: float = 1.0) -> Workload:
+def with_fp8_pool(wl: Workload, k_scale: float = 1.0, v_scale: float = 1.0, codes: str = "normal") -> Workload:
     """The same workload over an 8-bit pool: q, k, v and out keep ``dtype`` (bf16);
-    cached context is drawn as E4M3 codes; new tokens are quantized by the KV write."""
+    cached context is drawn as E4M3 codes (``codes``: "normal" or the heavier-
+    tailed "band"); new tokens are quantized by the KV write."""
     assert wl.dtype == "bf16", "8-bit pools are read by the bf16 compute path"
+    assert codes in ("normal", "band")
     return dataclasses.replace(wl, name=wl.name.replace("_bf16", "") + "_fp8kv", kv_dtype="fp8",
-                               k_scale=float(np.float32(k_scale)), v_scale=float(np.float32(v_scale)))
+                               k_scale=float(np.float32(k_scale)), v_scale=float(np.float32(v_scale)),
+                               fp8_codes=codes)

@@ -122,6 +122,11 @@ def _fp8_codes() -> np.ndarray:
 
 
 FP8_CODES = _fp8_codes()
+# A heavier-tailed alternative: the low byte picks one of the 56 codes 0x18 ..
+# 0x4F (magnitudes 1/16 .. 3.75) with equal probability, bit 15 the sign. It
+# puts far more mass near the top of the range than N(0, 1) does, which makes
+# softmax rows spikier; kept to track the bf16 rounding margin on such rows.
+FP8_CODES_BAND = (((np.arange(65536) >> 8) & 0x80) | (0x18 + (np.arange(65536) & 0xFF) % 56)).astype(np.uint8)
 CANARY_FP8 = 0x7F
 
 # NaN canaries for pool memory that a correct kernel never reads.
