@@ -203,6 +203,29 @@ pa_status pa_step_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor*
                       size_t workspace_bytes, pa_stream stream);
 
 /*
+ * pa_step without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. It computes what pa_step computes, with the same
+ * arguments minus the workspace, and calls no allocating routine of any
+ * library. Its scratch space is a fixed array of PA_NOALLOC_SCRATCH_BYTES in
+ * the library's device memory, one per GPU, held until the process ends.
+ *  - A step whose pa_attention_workspace_size() exceeds
+ *    PA_NOALLOC_SCRATCH_BYTES is rejected with PA_ERR_WORKSPACE before
+ *    anything is launched (use pa_step with a workspace then).
+ *  - Every launch stays on `stream`: no stream or event of the library's own
+ *    is created or used (large mixed batches run their prefill after the
+ *    decode instead of beside it).
+ *  - All calls on one GPU share its array, so calls that overlap in time on
+ *    one GPU (two streams, two host threads) race; serialise them.
+ *  - The array needs no initialisation: every call rewrites what it reads.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_step_noalloc(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                          const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                          const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                          const pa_tensor* context_lens, float scale, pa_stream stream);
+
+/*
  * Bytes of workspace pa_attention / pa_step need for these extents (the
  * split-K partial results, one set per new token of the sequences the decode
  * kernel attends -- those whose query length times Hq / Hkv is at most 16 --

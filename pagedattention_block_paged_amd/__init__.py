@@ -11,6 +11,8 @@ Calls (same names and argument order as the C ABI):
   seq_lens, context_lens, scale, out=None, workspace=None) -> out``
 - ``step(q, k, v, key_cache, value_cache, slot_mapping, block_tables,
   query_start_loc, seq_lens, context_lens, scale, out=None, workspace=None)``
+- ``step_noalloc(...)``: ``step`` without a workspace argument, on the
+  library's fixed per-GPU scratch (for callers that cannot allocate)
 
 KV pool layout: ``pool = new_kv_pool(num_blocks, num_kv_heads, head_size)``
 has shape ``[num_blocks, 2, 16, num_kv_heads, head_size]``; ``pool[:, 0]`` is
@@ -35,8 +37,8 @@ STATUS = {
     10: "PA_ERR_CONTENTS",
 }
 EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
-           "pa_step_fp8", "pa_attention_workspace_size", "pa_partition_tokens", "pa_status_string", "pa_last_error",
-           "pa_version")
+           "pa_step_fp8", "pa_step_noalloc", "pa_attention_workspace_size", "pa_partition_tokens", "pa_status_string",
+           "pa_last_error", "pa_version")
 PROFILE_EXPORTS = ("pa_profile_start", "pa_profile_stop", "pa_profile_kernel", "pa_profile_kernel_name")
 KERNELS = ("kv_write", "decode", "partition_reduce", "prefill_plan", "prefill")
 
@@ -78,8 +80,9 @@ def _load():
     lib.pa_reshape_and_cache_fp8.argtypes = [P, P, P, P, P, f32, f32, vp]
     lib.pa_attention_fp8.argtypes = [P, P, P, P, P, P, P, P, f32, f32, f32, vp, sz, vp]
     lib.pa_step_fp8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, f32, f32, f32, vp, sz, vp]
+    lib.pa_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, f32, vp]
     for f in ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
-              "pa_step_fp8"):
+              "pa_step_fp8", "pa_step_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.pa_attention_workspace_size.argtypes = [i64] * 6
     lib.pa_attention_workspace_size.restype = sz
@@ -198,6 +201,23 @@ def step(q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_star
                                 query_start_loc, seq_lens, context_lens)]
     _check(lib.pa_step(*[_ptr(d) for d in ds], ctypes.c_float(scale), ctypes.c_void_p(ws.data_ptr()),
                        ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
+
+
+def step_noalloc(q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
+                 context_lens, scale: float, out=None):
+    """pa_step_noalloc: pa_step with the library's fixed per-GPU scratch as its
+    workspace (nothing is allocated on the device by the call; `out` is
+    allocated here only if it is not given)."""
+    import torch
+
+    out = torch.empty_like(q) if out is None else out
+    ds = [describe(x) for x in (out, q, k, v, key_cache, value_cache, slot_mapping, block_tables,
+                                query_start_loc, seq_lens, context_lens)]
+    _check(lib.pa_step_noalloc(*[_ptr(d) for d in ds], ctypes.c_float(scale), _stream(q)))
     return out
 
 

@@ -388,9 +388,9 @@ bool prefill_beside_decode(const pa::AttnArgs& a) {
 // bf16 the prefill runs on a second stream, forked from and joined back into
 // `stream`, on a few CUs chosen by the plan kernel while the decode streams
 // on the rest; otherwise the two run one after the other on `stream`.
-pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream) {
+pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream, bool allow_side = true) {
   if (a.S == 0 || a.T == 0) return PA_OK;
-  SideStream* side = prefill_beside_decode(a) ? side_stream_for(stream) : nullptr;
+  SideStream* side = allow_side && prefill_beside_decode(a) ? side_stream_for(stream) : nullptr;
   if (!side) {
     PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
     PA_TRY(hip_status(pa::launch_prefill(a, stream, false), "prefill launch"));
@@ -548,11 +548,15 @@ pa_status attention_impl(const pa_tensor* out, const pa_tensor* q, const pa_tens
   return ok();
 }
 
+}  // namespace
+
+namespace pa {
+
 pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
                     const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
                     const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
                     const pa_tensor* context_lens, float scale, bool fp8, float k_scale, float v_scale,
-                    void* workspace, size_t workspace_bytes, pa_stream stream) {
+                    void* workspace, size_t workspace_bytes, pa_stream stream, bool allow_side) {
   pa::WriteArgs w{};
   pa::AttnArgs a{};
   PA_TRY(validate_write(k, v, key_cache, value_cache, slot_mapping, fp8, k_scale, v_scale, &w));
@@ -566,11 +570,12 @@ pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k
     PA_TRY(check_attention_contents(a, s));
   }
   if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
-  PA_TRY(run_attention(a, s));
+  PA_TRY(run_attention(a, s, allow_side));
   return ok();
 }
 
-}  // namespace
+}  // namespace pa
+
 
 extern "C" {
 
@@ -592,8 +597,8 @@ pa_status pa_step(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, 
                   const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
                   const pa_tensor* context_lens, float scale, void* workspace, size_t workspace_bytes,
                   pa_stream stream) {
-  return step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
-                   context_lens, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+  return pa::step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
+                       context_lens, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream, true);
 }
 
 pa_status pa_reshape_and_cache_fp8(const pa_tensor* k, const pa_tensor* v, const pa_tensor* key_cache,
@@ -616,8 +621,8 @@ pa_status pa_step_fp8(const pa_tensor* out, const pa_tensor* q, const pa_tensor*
                       const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
                       const pa_tensor* context_lens, float scale, float k_scale, float v_scale, void* workspace,
                       size_t workspace_bytes, pa_stream stream) {
-  return step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
-                   context_lens, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
+  return pa::step_impl(out, q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_start_loc, seq_lens,
+                       context_lens, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream, true);
 }
 
 size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads, int64_t num_kv_heads,

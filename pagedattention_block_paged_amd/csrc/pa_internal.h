@@ -117,6 +117,14 @@ struct ProfileScope {
   }
 };
 
+// pa_step / pa_step_fp8 (pa_api.cpp). allow_side = false keeps every launch
+// on `stream` (no stream or event of the library's own is created or used).
+pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                    const pa_tensor* key_cache, const pa_tensor* value_cache, const pa_tensor* slot_mapping,
+                    const pa_tensor* block_tables, const pa_tensor* query_start_loc, const pa_tensor* seq_lens,
+                    const pa_tensor* context_lens, float scale, bool fp8, float k_scale, float v_scale,
+                    void* workspace, size_t workspace_bytes, pa_stream stream, bool allow_side);
+
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // Decode kernel, then the partition reduce (decode.hip).
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);

@@ -271,3 +271,15 @@ def test_fp8_pool_validation():
     assert write_fp8(c) == PA_OK  # accepted; an empty batch launches nothing
     c.k = desc([0, 2, 64], I32)
     assert write_fp8(c) == PA_ERR_DTYPE
+
+
+def test_step_noalloc_without_a_gpu_reports_an_error():
+    """On a machine with no GPU the allocation-free step reports PA_ERR_HIP
+    (it looks up the stream's device first) instead of touching memory."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the GPU tests cover pa_step_noalloc")
+    d = Tensor()
+    rc = lib.pa_step_noalloc(*([ctypes.byref(d)] * 11), ctypes.c_float(0.125), None)
+    assert rc == 7 and b"pa_step_noalloc" in lib.pa_last_error()
