@@ -15,13 +15,17 @@ chunks of 512 tokens (prior contexts uniform in [0, 4096]) in one flattened
 batch of 8192 tokens, 32/8 heads, head size 128, bf16 -- the one workload that
 runs every part of the path. `value` is its decode KV-read bandwidth over the
 whole step; the line also carries mixed-step tokens/s, prefill TFLOP/s and the
-roofline of the decode (HBM) and prefill (bf16 MFMA) kernels. In this step the
-library runs the prefill kernel beside the decode kernel on a few CUs, so the
-prefill roofline is timed on the same chunks run alone. `secondary`
-holds the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode, the
-shared-prefix decode and a speculative-decode verification batch (4 new
-tokens per sequence over long contexts), each also timed as one HIP-graph replay per step
-(`ms_per_step_graph`).
+roofline of the decode (HBM) and prefill (bf16 MFMA, nested as
+roofline.prefill) kernels. In this step the library runs the prefill kernel
+beside the decode kernel on a few CUs, so the prefill roofline is timed on the
+same chunks run alone. `secondary` holds the other workloads -- the tiny fp32
+decode, the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode, the
+shared-prefix decode, a speculative-decode verification batch (4 new tokens
+per sequence over long contexts) and the 70B decode and 8B mixed step over an
+8-bit pool -- each over 20 timed steps (mean, median, min) and also timed as
+one HIP-graph replay per step (`ms_per_step_graph`). The decode's fraction is
+quoted against the 8 TB/s spec and against a non-temporal read probe run on
+the same GPU. `cpu_baseline` times the oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -99,6 +103,22 @@ def kernel_work(wl, dec, pre):
     q = int(n[dec].sum()) * wl.num_q_heads * wl.head_size * es
     pairs = int((n[pre] * C[pre] + n[pre] * (n[pre] + 1) // 2).sum())  # sum over queries of visible keys
     return kv + tables + q, 4 * wl.head_size * wl.num_q_heads * pairs
+
+
+def unique_decode_bytes(wl, dec):
+    """K/V bytes of the distinct blocks the decode kernel's sequences read (a
+    shared block once), plus their table entries and query rows."""
+    import numpy as np
+
+    import workloads as W
+
+    blocks = set()
+    for s in np.nonzero(dec)[0]:
+        blocks.update(wl.block_tables[s, : wl.blocks_used(s)].tolist())
+    L = wl.seq_lens[dec].astype(np.int64)
+    tables = int((-(-L // W.BLOCK_SIZE)).sum()) * 4
+    q = int(wl.query_lens[dec].astype(np.int64).sum()) * wl.num_q_heads * wl.head_size * W.DTYPE_BYTES[wl.dtype]
+    return len(blocks) * wl.block_bytes + tables + q
 
 
 def run_step(pa, wl, c, out, ws):
@@ -230,7 +250,20 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         d = kern["decode"]["avg_ms"]
         r["decode_kernel_bytes"] = dec_kernel_bytes
         r["decode_kernel_gbs"] = dec_kernel_bytes / (d * 1e-3) / 1e9
-        r["decode_kernel_hbm_frac"] = r["decode_kernel_gbs"] / HBM_PEAK_GBS
+        if int(wl.shared_len.max()) > 0:
+            # Shared prefix blocks are counted once per sequence that reads
+            # them: a logical rate, which may exceed the HBM peak because the
+            # shared blocks are re-read from the caches. The DRAM rate comes
+            # from the committed FETCH_SIZE / WRITE_SIZE counters of this
+            # kernel on this workload (null once the kernel source changed).
+            r["decode_kernel_gbs_logical"] = r.pop("decode_kernel_gbs")
+            r["decode_kernel_unique_bytes"] = unique_decode_bytes(wl, dec_set)
+            dram = kernel_traffic("decode", wl.name)
+            r["decode_kernel_dram_bytes"] = dram
+            r["decode_kernel_dram_gbs"] = None if dram is None else dram / (d * 1e-3) / 1e9
+            r["decode_kernel_dram_frac"] = None if dram is None else r["decode_kernel_dram_gbs"] / HBM_PEAK_GBS
+        else:
+            r["decode_kernel_hbm_frac"] = r["decode_kernel_gbs"] / HBM_PEAK_GBS
     if flops and "prefill" in kern:
         p = alone["prefill_ms"] if alone else kern["prefill"]["avg_ms"]
         r["prefill_tflops"] = flops / (p * 1e-3) / 1e12
@@ -311,13 +344,44 @@ def host_inputs(wl):
     return h(W.pool_device(wl, "cuda")), h(k), h(v), h(W.q_device(wl, "cuda"))
 
 
-def cpu_baseline(cfg: int, budget_s: float) -> dict:
-    """The oracle, as is, on the host cores, over a bounded sample of the workload.
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    Decode: a seeded sample of the workload's decode sequences (KV write +
-    attention), repeated until `budget_s` has passed; reported as decode
-    KV-read GB/s. Prefill: the workload's longest prefill chunk, once, as
-    GFLOP/s (fp64).
+
+def oracle_step(wl, threads: int = 0, reps: int = 1):
+    """The oracle's whole step (KV write + attention) on a workload's host
+    inputs, median wall time of `reps` runs (input generation excluded).
+    Returns (seconds, threads used)."""
+    import oracle
+
+    pool0, k, v, q = host_inputs(wl)
+    times, used = [], 0
+    for _ in range(reps):
+        pool = pool0.copy()
+        t0 = time.perf_counter()
+        oracle.reshape_and_cache(k, v, pool, wl.slot_mapping, wl.dtype)
+        _, used = oracle.attention(q, pool, wl.block_tables, wl.query_start_loc, wl.seq_lens, wl.context_lens,
+                                   wl.scale, wl.dtype, num_threads=threads, return_threads=True)
+        times.append(time.perf_counter() - t0)
+    return sorted(times)[len(times) // 2], used
+
+
+def cpu_baseline(cfg: int, budget_s: float) -> dict:
+    """The oracle, as is, on the host cores.
+
+    Headline: a seeded sample of the workload's decode sequences (KV write +
+    attention) repeated until `budget_s` has passed, as decode KV-read GB/s,
+    and the longest prefill chunk once, as GFLOP/s (fp64); with the whole
+    batch's time extrapolated from those two rates. Then whole batches: the
+    tiny fp32 and TinyLlama decode batches on one thread and on all (median
+    of 3), and the 70B 32k decode batch on all threads once.
     """
     import numpy as np
 
@@ -329,7 +393,8 @@ def cpu_baseline(cfg: int, budget_s: float) -> dict:
     pre = np.nonzero(~wl.decode_mask())[0]
     rs = np.random.default_rng(7)
     take = dec if dec.size <= 128 else np.sort(rs.choice(dec, size=128, replace=False))
-    out = {"unit": "GB/s", "kind": "oracle"}
+    out = {"unit": "GB/s", "kind": "oracle", "cpu_model": cpu_model(),
+           "affinity_cpus": len(os.sched_getaffinity(0))}
     if take.size:
         sub = W.sub_workload(wl, take)
         pool0, k, v, q = host_inputs(sub)
@@ -353,16 +418,34 @@ def cpu_baseline(cfg: int, budget_s: float) -> dict:
     if pre.size:
         s = int(pre[np.argmax(wl.seq_lens[pre])])
         sub = W.sub_workload(wl, [s])
-        pool, k, v, q = host_inputs(sub)
-        t0 = time.perf_counter()
-        oracle.reshape_and_cache(k, v, pool, sub.slot_mapping, sub.dtype)
-        _, threads = oracle.attention(q, pool, sub.block_tables, sub.query_start_loc, sub.seq_lens, sub.context_lens,
-                                      sub.scale, sub.dtype, return_threads=True)
-        secs = time.perf_counter() - t0
+        secs, threads = oracle_step(sub)
         out["prefill_gflops"] = sub.prefill_flops() / secs / 1e9
         out["prefill_sample"] = (f"longest prefill chunk ({int(sub.query_lens[0])} tokens after "
                                  f"{int(sub.context_lens[0])} cached), once, {secs:.2f} s, {threads} threads")
         out.setdefault("cores", threads)
+    if take.size and pre.size:
+        # the whole batch at the sample's rates: decode bytes / decode rate +
+        # prefill FLOPs / prefill rate
+        est = wl.decode_bytes() / (out["value"] * 1e9) + wl.prefill_flops() / (out["prefill_gflops"] * 1e9)
+        out["whole_batch_estimate_s"] = est
+        out["whole_batch_tokens_per_s_estimate"] = wl.num_tokens / est
+        out["whole_batch_note"] = ("estimated, not run: the decode sample's GB/s applied to the batch's "
+                                   f"{wl.decode_bytes() / 1e9:.1f} GB of decode bytes plus the chunk's GFLOP/s "
+                                   f"applied to its {wl.prefill_flops() / 1e9:.1f} GFLOP of prefill")
+    runs = {}
+    for c, one in ((1, True), (2, True), (4, False)):
+        full = W.config_workload(c)
+        # the same sequences over a compact pool (only the blocks they use)
+        w = W.sub_workload(full, np.arange(full.num_seqs))
+        row = {"workload": full.name}
+        for thr in ((1, 0) if one else (0,)):
+            secs, used = oracle_step(w, threads=thr, reps=3 if one else 1)
+            row[f"threads_{used}"] = {"seconds": secs, "decode_gbs": w.decode_bytes() / secs / 1e9,
+                                      "tokens_per_s": w.num_tokens / secs,
+                                      "runs": "median of 3" if one else "once"}
+        runs[full.name] = row
+        log(f"[bench] cpu baseline {full.name}: {row}")
+    out["whole_batches"] = runs
     return out
 
 
@@ -447,27 +530,29 @@ def prefill_timing_note(head: dict) -> str:
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 
-def copy_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> float:
-    """What a plain device-to-device copy reaches on this GPU, in GB/s (bytes
-    read plus bytes written), best of `reps`: the practical HBM ceiling that
-    the decode's fraction is also quoted against."""
+def read_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> float:
+    """What a plain non-temporal read stream reaches on this GPU, in GB/s,
+    best of `reps` over 1 GiB (the library's pa_profile_read_probe: every byte
+    read once with 16-byte non-temporal loads, as the decode reads K/V): the
+    practical ceiling of a read-bound kernel, beside the 8 TB/s spec."""
     import torch
 
-    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
+    import pagedattention_block_paged_amd as pa
+
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     for _ in range(2):
-        dst.copy_(src)
+        pa.read_probe(buf)
     best = float("inf")
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        dst.copy_(src)
+        pa.read_probe(buf)
         e1.record()
         e1.synchronize()
         best = min(best, e0.elapsed_time(e1) * 1e-3)
-    del src, dst
+    del buf
     torch.cuda.empty_cache()
-    return 2 * nbytes / best / 1e9
+    return nbytes / best / 1e9
 
 
 def main():
@@ -475,9 +560,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
-    ap.add_argument("--secondary", default="2,4,5,6,7,8", help="other workloads to measure, or 'none'")
-    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-8)")
+    ap.add_argument("--secondary", default="1,2,4,5,6,7,8", help="other workloads to measure, or 'none'")
+    ap.add_argument("--secondary-steps", type=int, default=20)
+    ap.add_argument("--secondary-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-host-manager", action="store_true",
                     help="skip timing the host KV block manager on the headline batch")
@@ -505,11 +591,11 @@ def main():
         for cfg in [int(x) for x in args.secondary.split(",") if x]:
             if cfg == args.config:
                 continue
-            r = measure(cfg, args.secondary_steps, 1, flush=args.flush, graph=not args.no_graph)
+            r = measure(cfg, args.secondary_steps, args.secondary_warmup, flush=args.flush, graph=not args.no_graph)
             log(f"[bench] cfg {cfg}: {json.dumps(r)}")
             secondary[r["workload"]] = r
-    copy_gbs = copy_bandwidth()
-    log(f"[bench] device copy: {copy_gbs:.1f} GB/s (read + write of 1 GiB, best of 10)")
+    read_gbs = read_bandwidth()
+    log(f"[bench] read probe: {read_gbs:.1f} GB/s (non-temporal read of 1 GiB, best of 10)")
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -528,6 +614,7 @@ def main():
 
     dec = head.get("decode_kernel_gbs")
     pre = head.get("prefill_tflops")
+    pre_peak = head.get("prefill_mfma_peak", BF16_PEAK_TFLOPS)
     line = {
         "metric": METRIC,
         "value": head["decode_gbs_step"],
@@ -553,6 +640,8 @@ def main():
             "parallelism": "single GPU",
         },
         "value_definition": "decode KV-read bytes (K, V, block tables, q) per whole pa_step, divided by the step time",
+        "ms_per_step_median": head["ms_per_step_median"],
+        "ms_per_step_min": head["ms_per_step_min"],
         "hbm_frac_step": head["decode_gbs_step"] / HBM_PEAK_GBS,
         "mixed_step_tokens_per_s": head["tokens_per_s"],
         "prefill_tflops": pre,
@@ -563,21 +652,22 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": (dec / HBM_PEAK_GBS) if dec else None,
-            "copy_gbs": copy_gbs,
-            "frac_of_copy": (dec / copy_gbs) if dec else None,
             "traffic": kernel_traffic("decode", head["workload"]),
             "algorithmic_bytes": head.get("decode_kernel_bytes"),
-        },
-        "roofline_prefill": None if pre is None else {
-            "kernel": "prefill",
-            "bound": "mfma",
-            "achieved": pre,
-            "peak": head.get("prefill_mfma_peak", BF16_PEAK_TFLOPS),
-            "unit": "TFLOP/s",
-            "frac": pre / head.get("prefill_mfma_peak", BF16_PEAK_TFLOPS),
-            "traffic": kernel_traffic("prefill", head["workload"]),
-            "algorithmic_flops": head["prefill_flops"],
-            "timed": prefill_timing_note(head),
+            "read_probe_gbs": read_gbs,
+            "frac_of_read_probe": (dec / read_gbs) if dec else None,
+            "prefill": None if pre is None else {
+                "kernel": "prefill",
+                "bound": "mfma",
+                "achieved": pre,
+                "peak": pre_peak,
+                "unit": "TFLOP/s",
+                "frac": pre / pre_peak,
+                "traffic": kernel_traffic("prefill", head["workload"]),
+                "algorithmic_flops": head["prefill_flops"],
+                "kernel_ms": (head.get("prefill_alone") or {}).get("prefill_ms"),
+                "timed": prefill_timing_note(head),
+            },
         },
         "cpu_baseline": cpu,
         "host_kv_manager": mgr,

@@ -35,6 +35,14 @@ int pa_profile_kernel(int id, double* total_ms, int64_t* launches);
 /* Name of kernel `id` ("" for an unknown id). */
 const char* pa_profile_kernel_name(int id);
 
+/* Launch, on `stream` (a hipStream_t), one read of every byte of the device
+ * buffer `buf` with non-temporal 16-byte loads, as the decode reads K/V;
+ * nothing is written. Time it with events around the call to measure the
+ * GPU's sustained read bandwidth. `buf` 16-byte aligned, `bytes` a multiple
+ * of 16. Returns 0, PA_ERR_SHAPE (3) for a bad buffer, PA_ERR_HIP (7) if the
+ * launch fails. */
+int pa_profile_read_probe(const void* buf, uint64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,7 +39,8 @@ STATUS = {
 EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_cache_fp8", "pa_attention_fp8",
            "pa_step_fp8", "pa_step_noalloc", "pa_attention_workspace_size", "pa_partition_tokens", "pa_status_string",
            "pa_last_error", "pa_version")
-PROFILE_EXPORTS = ("pa_profile_start", "pa_profile_stop", "pa_profile_kernel", "pa_profile_kernel_name")
+PROFILE_EXPORTS = ("pa_profile_start", "pa_profile_stop", "pa_profile_kernel", "pa_profile_kernel_name",
+                   "pa_profile_read_probe")
 KERNELS = ("kv_write", "decode", "partition_reduce", "prefill_plan", "prefill")
 
 
@@ -99,6 +100,8 @@ def _load():
     lib.pa_profile_kernel.restype = ctypes.c_int
     lib.pa_profile_kernel_name.argtypes = [ctypes.c_int]
     lib.pa_profile_kernel_name.restype = ctypes.c_char_p
+    lib.pa_profile_read_probe.argtypes = [vp, ctypes.c_uint64, vp]
+    lib.pa_profile_read_probe.restype = ctypes.c_int
     return lib
 
 
@@ -254,6 +257,13 @@ def step_fp8(q, k, v, key_cache, value_cache, slot_mapping, block_tables, query_
                            ctypes.c_float(v_scale), ctypes.c_void_p(ws.data_ptr()),
                            ctypes.c_size_t(ws.numel() * ws.element_size()), _stream(q)))
     return out
+
+
+def read_probe(buf) -> None:
+    """One non-temporal read of every byte of the device tensor `buf` on the
+    current stream (pa_profile_read_probe): the GPU's plain read stream."""
+    _check(lib.pa_profile_read_probe(ctypes.c_void_p(buf.data_ptr()), ctypes.c_uint64(buf.numel() * buf.element_size()),
+                                     _stream(buf)))
 
 
 class profile:

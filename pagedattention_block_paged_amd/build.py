@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "profile.cpp", "kv_manager.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "noalloc.hip"]
+SOURCES = ["pa_api.cpp", "profile.cpp", "kv_manager.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "noalloc.hip", "probe.hip"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
 
