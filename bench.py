@@ -530,27 +530,32 @@ def prefill_timing_note(head: dict) -> str:
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 
-def read_bandwidth(nbytes: int = 1 << 30, reps: int = 10) -> float:
+def read_bandwidth(nbytes: int = 4 << 30, reps: int = 10) -> float:
     """What a plain non-temporal read stream reaches on this GPU, in GB/s,
-    best of `reps` over 1 GiB (the library's pa_profile_read_probe: every byte
+    best of `reps` over 4 GiB (the library's pa_profile_read_probe: every byte
     read once with 16-byte non-temporal loads, as the decode reads K/V): the
-    practical ceiling of a read-bound kernel, beside the 8 TB/s spec."""
+    practical ceiling of a read-bound kernel, beside the 8 TB/s spec. A 2 GiB
+    read queued ahead of each timed probe keeps the host's launch latency
+    out of the timed interval, as the cache flush does for the steps."""
     import torch
 
     import pagedattention_block_paged_amd as pa
 
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    ahead = torch.ones(2 << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int64, device="cuda")
     for _ in range(2):
         pa.read_probe(buf)
     best = float("inf")
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.sum(ahead.view(torch.int64), dim=0, keepdim=True, out=sink)
         e0.record()
         pa.read_probe(buf)
         e1.record()
         e1.synchronize()
         best = min(best, e0.elapsed_time(e1) * 1e-3)
-    del buf
+    del buf, ahead
     torch.cuda.empty_cache()
     return nbytes / best / 1e9
 
@@ -595,7 +600,7 @@ def main():
             log(f"[bench] cfg {cfg}: {json.dumps(r)}")
             secondary[r["workload"]] = r
     read_gbs = read_bandwidth()
-    log(f"[bench] read probe: {read_gbs:.1f} GB/s (non-temporal read of 1 GiB, best of 10)")
+    log(f"[bench] read probe: {read_gbs:.1f} GB/s (non-temporal read of 4 GiB, best of 10)")
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -7,7 +7,9 @@
  * no event is created or recorded.
  *
  * Kernel ids: 0 KV write, 1 decode (split-K partitions), 2 partition reduce,
- * 3 prefill plan, 4 chunked prefill.
+ * 3 prefill plan, 4 chunked prefill (which also combines the decode's
+ * partitions when it runs after the decode on the launch stream), 5 KV write
+ * and plan in one launch (steps whose prefill runs after the decode).
  */
 #ifndef PA_PROFILE_H_
 #define PA_PROFILE_H_
@@ -18,7 +20,7 @@
 extern "C" {
 #endif
 
-#define PA_PROFILE_KERNELS 5
+#define PA_PROFILE_KERNELS 6
 
 /* Drop earlier records and start recording. Returns 0 (PA_OK). */
 int pa_profile_start(void);

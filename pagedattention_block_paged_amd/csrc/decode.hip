@@ -1,40 +1,42 @@
-// Decode attention: sequences with exactly one new token read all of their
-// cached K/V through the block table; HBM-bound ("Inside vLLM", section
-// "Scheduler": decode steps are memory-bandwidth-bound; ngrok "Serving models
-// at scale with vLLM", section "Speculative decoding": a decode pass is
-// limited by moving data, not by math).
+// Decode attention: sequences whose new tokens times the query heads per KV
+// head fit 16 MFMA columns (every decode, and short queries such as
+// speculative-decode verification) read all of their cached K/V through the
+// block table; HBM-bound ("Inside vLLM", section "Scheduler": decode steps
+// are memory-bandwidth-bound; "Serving models at scale with vLLM", section
+// "Speculative decoding": a decode pass is limited by moving data, not math).
 //
 // Design for gfx950 (the pages give no kernel design):
-//  - A workgroup owns (sequence s, KV head g, partition p), the keys
-//    [p * PT, min((p + 1) * PT, L)). Its 4 waves take the partition's 16-token
-//    blocks round-robin, so neighbouring waves stream neighbouring blocks,
-//    and merge their partial softmax states through LDS at the end. All
-//    G = Hq / Hkv query heads of the group share each K/V read.
-//  - Scores use MFMA with the key rows as the A operand: S^T = K . Q^T. Each
-//    lane loads the 16-byte K chunk it feeds the matrix core straight from
-//    HBM. Query heads fill the 16 columns (G <= 16; unused columns are zero
-//    and cost nothing in an HBM-bound kernel).
-//  - In the score layout a lane holds one head column and 4 consecutive key
-//    rows, which is already the P^T operand of the 16x16x16 bf16 MFMA. V needs
-//    keys contiguous per lane instead of d, so each wave transposes its block
-//    of V through a private LDS tile (8-byte writes and reads, no barrier),
-//    and O^T = V^T . P^T runs in bf16 with fp32 accumulation. Each lane then
-//    owns one head column of O^T, so rescaling needs no lane exchange.
-//    fp32 inputs keep an exact path: V widened, P.V on the fp32 16x16x4 MFMA.
+//  - A workgroup of 8 waves owns (sequence s, group of hw KV heads, partition
+//    p), the keys [p * PT, min((p + 1) * PT, L)). With 8 KV heads each wave
+//    streams one head through every block of the partition, so the 8 head
+//    slices of a pool block (one contiguous block of all heads) are read by
+//    one workgroup at about the same time; with fewer heads the 8 / hw waves
+//    of a head split the blocks round-robin and merge through LDS at the end.
+//    All G = Hq / Hkv query heads of a KV head share each K/V read.
+//  - Each lane loads the 16-byte chunks of a block's K and V head slices it
+//    needs with non-temporal buffer loads (one block in flight per wave), then
+//    stages them through a per-wave LDS tile into the MFMA operand layouts
+//    (8-bit codes are widened to bf16 on the way into LDS).
+//  - Scores use MFMA with the key rows as the A operand: S^T = K . Q^T; the
+//    16 columns are (new token, query head) pairs, each with its own causal
+//    limit. In the score layout a lane holds one column and 4 consecutive
+//    keys, which is already the P^T operand of the 16x16x16 bf16 MFMA; V^T
+//    comes from the row-major V slice through the transposing LDS read, so
+//    O^T = V^T . P^T needs no lane exchange and rescaling touches one column
+//    per lane. fp32 inputs keep an exact path on the fp32 MFMA.
 //  - Online softmax in log2 units with a lazy rescale: the running maximum is
 //    only raised (and the accumulators rescaled) when a block's maximum beats
 //    it by more than 2^8, so weights stay <= 256 and rescales are rare.
-//  - Each wave can keep NPF blocks of K and V in flight in registers (a ring
-//    of static slots). One slot measures best: the occupancy it leaves hides
-//    HBM latency better than deeper rings.
 //  - Sequences longer than one partition write (unnormalised output, max,
-//    weight sum) per partition; a second kernel combines partitions in a fixed
-//    order (deterministic). Single-partition sequences write the output
-//    directly.
+//    weight sum) per partition; the partitions are combined in a fixed order
+//    (deterministic) by a reduce kernel, or by the prefill kernel's waves
+//    when it runs after the decode on the same stream. Single-partition
+//    sequences write the output directly.
 #include <cstdlib>
 #include <type_traits>
 
 #include "pa_internal.h"
+#include "step_parts.h"
 
 namespace pa {
 namespace {
@@ -48,7 +50,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr size_t kDecodeMaxLds = 80 * 1024;  // dynamic LDS a decode workgroup may ask for
-constexpr size_t kDecodeRingMaxLds = 128 * 1024;  // the largest ring (8 waves x 2 stages x 8 KB)
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
@@ -509,343 +510,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   combine_waves<BF16, D, KV8>(a, smem, wstride, hw, wph, ncol, hg, G, q0, nparts, p);
 }
 
-// ------------------------------------------------------- bf16 pool, LDS ring --
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const u32x4 lds_cu32x4;
-
-// Wait until at most N vector-memory operations of this wave are in flight.
-// The memory clobber keeps the compiler from moving memory accesses across it.
-template <int N>
-__device__ inline void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// 16 bytes per lane straight into LDS: lane l's bytes land at dst + 16 l (dst
-// is wave-uniform). An offset at or past the resource's size reads zeros.
-__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t off, lds_char* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(dst), 16, off, 0, 0, kStreamPolicy);
-}
-
-// One stage of a wave's ring: one block's K slice of the wave's KV head (16
-// rows of D bf16), then its V slice, in the layouts the fragment reads of
-// the register-staged path use (chunk c of row r at c ^ swz(r)).
-template <int D>
-struct RingStage {
-  static constexpr int ROWB = D * 2;                  // bytes of one row's head slice
-  static constexpr int LPR = ROWB / 16;               // lanes per row in a load (8 or 16)
-  static constexpr int RPI = 64 / LPR;                // rows per load instruction (8 or 4)
-  static constexpr int LPH = kBlockTokens / RPI;      // load instructions per K (or V) slice
-  static constexpr int HALF = kBlockTokens * ROWB;    // bytes of a K (or V) slice
-  static constexpr int BYTES = 2 * HALF;
-  static constexpr int LOADS = 2 * LPH;               // vector-memory operations per block
-  using Sh = DecodeShape<true, D>;
-  __device__ static int k_off(int r, int c) { return Sh::kt_off(r, c); }
-  __device__ static int v_off(int r, int e) { return HALF + Sh::vt_off(r, e); }
-};
-
-// The sweep of one wave over its blocks with an NS-deep ring of LDS stages:
-// a block's K and V go from HBM straight into a stage (no registers hold data
-// in flight), NS blocks are requested ahead, and a stage is refilled as soon
-// as its block has been consumed. dma and rd are two views of the same LDS:
-// loads write through dma, fragment reads go through rd; a stage is never
-// read and loaded at once, and the restrict hint lets the compiler see that
-// (otherwise it waits for every load in flight before each LDS read).
-template <int D, int NS>
-__device__ __attribute__((always_inline)) inline void ring_sweep(
-    const AttnArgs& a, const int32_t* __restrict__ bt, lds_char* __restrict__ dma, const lds_char* __restrict__ rd,
-    int b0, int phase, int wph, int nbw, int L, int lim, int end, uint32_t g, const uint4 (&qv)[D / 32],
-    float qk_scale, f32x4 (&o)[D / 16], float& m_run, float& l_run) {
-  using St = RingStage<D>;
-  constexpr int KC = D / 32, NACC = D / 16;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, kg = lane >> 4;
-  const uint32_t NB = static_cast<uint32_t>(min(a.NB, int64_t(0x7fffffff)));
-  const char* kbase = a.kc + int64_t(g) * a.kc_sh;
-  const char* vbase = a.vc + int64_t(g) * a.vc_sh;
-  const uint32_t k_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.kc_sr + D * 2);
-  const uint32_t v_rec = static_cast<uint32_t>((kBlockTokens - 1) * a.vc_sr + D * 2);
-  // Load i of a slice covers rows RPI i .. RPI i + RPI - 1; lane l fills LDS
-  // chunk slot l % LPR of row RPI i + l / LPR, i.e. it fetches the row's
-  // logical chunk (l % LPR) ^ swz(row).
-  uint32_t koff[St::LPH], voff[St::LPH];
-  int row[St::LPH];
-#pragma unroll
-  for (int i = 0; i < St::LPH; ++i) {
-    row[i] = St::RPI * i + lane / St::LPR;
-    const int cs = lane % St::LPR;
-    koff[i] = static_cast<uint32_t>(row[i] * a.kc_sr + 16 * (cs ^ St::Sh::swzk(row[i])));
-    voff[i] = static_cast<uint32_t>(row[i] * a.vc_sr + 16 * (cs ^ St::Sh::swz(row[i])));
-  }
-  // Block ids of the wave's blocks (at most 128: a partition has at most
-  // 2048 tokens), one per lane in two registers, loaded before the sweep so
-  // that no load inside it makes the compiler wait for the ring (indices
-  // clamped into the table row: entries past the wave's blocks are unused).
-  auto ids_window = [&](int w) {
-    const int64_t j = int64_t(b0) + phase + int64_t(wph) * (64 * w + lane);
-    return bt[j < a.MB ? j : a.MB - 1];
-  };
-  int ids0 = ids_window(0), ids1 = ids_window(1);
-  asm volatile("" ::"v"(ids0), "v"(ids1));  // both have landed before the first request
-  // Request block ib of the wave into stage st. Past the wave's blocks every
-  // lane reads past the resource (zeros, no memory traffic), so each block
-  // issues the same number of loads and the waits below can count them.
-  auto request = [&](int st, int ib) {
-    const int idr = ib < 64 ? ids0 : ids1;
-    const uint32_t id = static_cast<uint32_t>(__builtin_amdgcn_readlane(idr, ib & 63));
-    const int64_t pid = id < NB ? int64_t(id) : 0;
-    const int blk = b0 + phase + wph * ib;
-    const int rows = ib < nbw ? min(kBlockTokens, L - blk * kBlockTokens) : 0;  // rows of the block inside L
-    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + pid * a.kc_sb, k_rec);
-    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + pid * a.vc_sb, v_rec);
-    lds_char* dst = dma + st * St::BYTES;
-#pragma unroll
-    for (int i = 0; i < St::LPH; ++i) load_lds16(kr, row[i] < rows ? koff[i] : 0x80000000u, dst + 1024 * i);
-#pragma unroll
-    for (int i = 0; i < St::LPH; ++i)
-      load_lds16(vr, row[i] < rows ? voff[i] : 0x80000000u, dst + St::HALF + 1024 * i);
-  };
-  // Per-lane fragment addresses within a stage: K row n at chunk 4c + kg
-  // (the A operand of k-step c); V^T of tile t through the transposing read
-  // (lane (kg, n) points at V[4kg + n/4][16t + 4(n%4) ..] and receives
-  // V[4kg + e][16t + n], e = 0..3).
-  uint32_t k_rd[KC], v_rd[NACC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) k_rd[c] = static_cast<uint32_t>(St::k_off(n, 4 * c + kg));
-#pragma unroll
-  for (int t = 0; t < NACC; ++t) v_rd[t] = static_cast<uint32_t>(St::v_off(4 * kg + (n >> 2), 16 * t + 4 * (n & 3)));
-
-  // Consume the block in stage st: scores S^T[token 4kg + r][column n], online
-  // softmax, O^T += V^T P^T. Rows past the sequence end hold zeros.
-  auto consume = [&](int st, int blk) {
-    const lds_char* sb = rd + st * St::BYTES;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      const u32x4 kc = *reinterpret_cast<lds_cu32x4*>(sb + k_rd[c]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc), __builtin_bit_cast(bf16x8, qv[c]),
-                                                     acc, 0, 0, 0);
-    }
-    float sc[4];
-    const int tok0 = blk * kBlockTokens + 4 * kg;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sc[r] = (tok0 + r < lim) ? acc[r] * qk_scale : -INFINITY;
-    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    // a column with no visible key yet keeps maximum -inf and weights 0
-    if (__any(mloc > m_run + kRescaleThreshold)) {
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = m_new == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < NACC; ++t) o[t] *= alpha;
-      m_run = m_new;
-    }
-    float pr[4];
-    const float m_ref = m_run == -INFINITY ? 0.f : m_run;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr[r] = fast_exp2(sc[r] - m_ref);
-      l_run += pr[r];
-    }
-    const i16x4 pb = __builtin_bit_cast(i16x4, make_uint2(pack_bf16(pr[0], pr[1]), pack_bf16(pr[2], pr[3])));
-#pragma unroll
-    for (int t = 0; t < NACC; ++t) {
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<lds_char*>(sb) + v_rd[t]));
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[t], 0, 0, 0);
-    }
-  };
-
-#pragma unroll
-  for (int j = 0; j < NS; ++j) request(j, j);
-  for (int i = 0; i < nbw; i += NS) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      const int ib = i + j;
-      if (ib < nbw) {
-        // stage j has landed once at most the NS - 1 later blocks' loads are in flight
-        wait_vmem<(NS - 1) * St::LOADS>();
-        consume(j, b0 + phase + wph * ib);
-        // the stage's fragment reads are done before it is refilled
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        request(j, ib + NS);
-      }
-    }
-  }
-  // No load may still be writing LDS when the stages are reused or freed.
-  wait_vmem<0>();
-}
-
-// bf16 pools: like decode_kernel (same grid and workgroups, same results up
-// to the order of fp32 additions), but each wave streams its blocks through an
-// NS-stage LDS ring. With one wave per KV head (8 heads per workgroup) the
-// waves store their results themselves and never wait for each other.
-template <int D, int NS>
-__global__ __launch_bounds__(kDecodeThreads) void decode_ring_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
-                                                                     int hw) {
-  using St = RingStage<D>;
-  constexpr int KC = D / 32, NACC = D / 16;
-  extern __shared__ uint4 lds_dyn[];
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 15, kg = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wph = kDecodeWaves / hw;  // waves per KV head
-  const uint32_t n_hg = static_cast<uint32_t>(a.Hkv / hw);
-  const uint32_t s = blockIdx.x / n_hg, hg = blockIdx.x - s * n_hg;
-  const uint32_t g = hg * hw + wave % hw;
-  const int phase = wave / hw;
-  const int p = blockIdx.y;
-  const int PT = static_cast<int>(a.part_tokens);
-  const int b0 = p * (PT / kBlockTokens);
-  const int32_t* bt = bt_all + int64_t(s) * a.bt_row;
-  const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
-  const int G = static_cast<int>(a.Hq / a.Hkv);
-  const int nq = q1 - q0;
-  if (!decode_path(nq, G) || q0 < 0 || q1 > a.T) return;  // whole workgroup
-  const int L = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
-  const int start = p * PT;
-  if (start >= L) return;  // whole workgroup
-  const int end = min(start + PT, L);
-  const int nparts = (L + PT - 1) / PT;
-  const int ncol = nq * G;
-  const int C = min(max(a.ctx_lens[s], 0), L);
-  const int lim = min(end, C + n / G + 1);
-  const float qk_scale = a.scale * kLog2e;
-  const int nblk = (end - start + kBlockTokens - 1) / kBlockTokens;
-  const int nbw = nblk > phase ? (nblk - phase + wph - 1) / wph : 0;
-
-  uint4 qv[KC];
-  {
-    const int qi = n < ncol ? n / G : 0, qh = n < ncol ? n % G : 0;
-    const char* qrow = a.q + int64_t(q0 + qi) * a.q_st + int64_t(g * G + qh) * a.q_sh + 16 * kg;
-#pragma unroll
-    for (int c = 0; c < KC; ++c)
-      qv[c] = n < ncol ? *reinterpret_cast<const uint4*>(qrow + 64 * c) : make_uint4(0, 0, 0, 0);
-  }
-  f32x4 o[NACC];
-#pragma unroll
-  for (int t = 0; t < NACC; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
-  {
-    // The load view is offset by an opaque zero so that the two views are
-    // distinct values (identical arguments would defeat the restrict hint).
-    uint32_t zero = 0;
-    asm volatile("" : "+s"(zero));
-    const uint32_t base = static_cast<uint32_t>(wave) * NS * St::BYTES;
-    ring_sweep<D, NS>(a, bt, (lds_char*)lds_dyn + base + zero,
-                      (const lds_char*)lds_dyn + base, b0, phase, wph, nbw, L, lim, end, g, qv,
-                      qk_scale, o, m_run, l_run);
-  }
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (wph == 1) {
-    // this wave alone holds its head's result: lane (kg, n) has column n,
-    // d = 16t + 4kg .. + 3
-    if (n < ncol) {
-      const int64_t hq = int64_t(g) * G + n % G;
-      const int64_t t = q0 + n / G;
-      if (nparts == 1) {
-        const float inv = 1.f / l_tot;
-        char* dst = a.out + t * a.out_st + hq * a.out_sh + 8 * kg;
-#pragma unroll
-        for (int u = 0; u < NACC; ++u)
-          *reinterpret_cast<uint2*>(dst + 32 * u) =
-              make_uint2(pack_bf16(o[u][0] * inv, o[u][1] * inv), pack_bf16(o[u][2] * inv, o[u][3] * inv));
-      } else {
-        const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
-#pragma unroll
-        for (int u = 0; u < NACC; ++u)
-          *reinterpret_cast<float4*>(a.ws_o + slot * D + 16 * u + 4 * kg) = make_float4(o[u][0], o[u][1], o[u][2], o[u][3]);
-        if (kg == 0) a.ws_ml[slot] = make_float2(m_run, l_tot);
-      }
-    }
-    return;
-  }
-  // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: ncol * D]
-  __syncthreads();  // every wave's ring is drained
-  float* smem = reinterpret_cast<float*>(lds_dyn);
-  const int wstride = 32 + ncol * D;
-  float* ws = smem + wave * wstride;
-  if (kg == 0) {
-    ws[n] = m_run;
-    ws[16 + n] = l_tot;
-  }
-  if (n < ncol) {
-#pragma unroll
-    for (int u = 0; u < NACC; ++u)
-      *reinterpret_cast<float4*>(ws + 32 + n * D + 16 * u + 4 * kg) = make_float4(o[u][0], o[u][1], o[u][2], o[u][3]);
-  }
-  __syncthreads();
-  combine_waves<true, D, false>(a, smem, wstride, hw, wph, ncol, hg, G, q0, nparts, p);
-}
-
-// Combine the partitions of multi-partition sequences of the decode kernel:
-// one wave per (sequence, query head), for each of the sequence's new tokens,
-// in fixed partition order.
+// Combine the partitions of multi-partition sequences of the decode kernel
+// (step_parts.h): one wave per (sequence, query head), in fixed partition
+// order.
 template <bool BF16, int D>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(AttnArgs a) {
-  constexpr int DPL = D / 64;  // output elements per lane
-  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * kWaves + wave;
-  const int64_t s = item / a.Hq, hq = item - s * a.Hq;
-  if (s >= a.S) return;
-  const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
-  if (!decode_path(q1 - q0, a.Hq / a.Hkv) || q0 < 0 || q1 > a.T) return;
-  const int64_t L = min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens);
-  const int nparts = static_cast<int>((L + a.part_tokens - 1) / a.part_tokens);
-  if (nparts <= 1) return;
-  for (int64_t t = q0; t < q1; ++t) {
-    const float2* ml = a.ws_ml + (t * a.Hq + hq) * a.max_parts;
-    const float* po = a.ws_o + (t * a.Hq + hq) * a.max_parts * D + DPL * lane;
-    float m = -INFINITY;
-    for (int p = lane; p < nparts; p += 64) m = fmaxf(m, ml[p].x);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float acc[DPL] = {};
-    float lsum = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += 64) {
-      float w = 0.f;
-      if (p0 + lane < nparts) {
-        const float2 v = ml[p0 + lane];
-        w = fast_exp2(v.x - m);
-        lsum += w * v.y;
-      }
-      const int cnt = min(64, nparts - p0);
-      for (int j = 0; j < cnt; ++j) {
-        const float wj = __shfl(w, j);
-        const float* x = po + int64_t(p0 + j) * D;
-        if constexpr (DPL == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(x);
-          acc[0] += wj * v.x;
-          acc[1] += wj * v.y;
-        } else {
-          acc[0] += wj * x[0];
-        }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off);
-    const float inv = 1.f / lsum;
-    char* dst = a.out + t * a.out_st + hq * a.out_sh;
-    if constexpr (BF16) {
-      if constexpr (DPL == 2) {
-        *reinterpret_cast<uint32_t*>(dst + 4 * lane) = pack_bf16(acc[0] * inv, acc[1] * inv);
-      } else {
-        reinterpret_cast<__bf16*>(dst)[lane] = static_cast<__bf16>(acc[0] * inv);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < DPL; ++i) reinterpret_cast<float*>(dst)[DPL * lane + i] = acc[i] * inv;
-    }
-  }
+  reduce_partitions<BF16, D>(a, static_cast<int64_t>(blockIdx.x) * kWaves + wave, threadIdx.x & 63);
 }
 
-hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream, bool bf16) {
+hipError_t reduce_launch(const AttnArgs& a, hipStream_t stream) {
   if (a.max_parts <= 1) return hipSuccess;
+  const bool bf16 = a.elem == Elem::BF16;  // bf16 out (also over an 8-bit pool)
   const dim3 grid(static_cast<unsigned>((a.S * a.Hq + kWaves - 1) / kWaves));
   ProfileScope ps(kReduce, stream);
   if (a.D == 64) {
@@ -858,9 +534,8 @@ hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream, bool bf16) {
   return hipGetLastError();
 }
 
-// fp32 and 8-bit pools: the register-staged kernel.
 template <bool BF16, int D, bool KV8>
-hipError_t launch_staged(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce) {
   using Sh = DecodeShape<BF16, D>;
   const int hw = decode_heads_per_workgroup(a.Hkv);
   const size_t merge = sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D);  // up to 16 columns
@@ -879,56 +554,20 @@ hipError_t launch_staged(const AttnArgs& a, hipStream_t stream) {
                        hw);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_reduce(a, stream, BF16);
-}
-
-// bf16 pools: the LDS-ring kernel with NS stages per wave.
-template <int D, int NS>
-hipError_t launch_ring(const AttnArgs& a, hipStream_t stream) {
-  using St = RingStage<D>;
-  const int hw = decode_heads_per_workgroup(a.Hkv);
-  const size_t ring = size_t(kDecodeWaves) * NS * St::BYTES;
-  const size_t merge = hw < kDecodeWaves ? sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D) : 0;
-  const size_t lds = ring > merge ? ring : merge;
-  static_assert(size_t(kDecodeWaves) * NS * St::BYTES <= kDecodeRingMaxLds, "ring exceeds the LDS of a CU");
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_ring_kernel<D, NS>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeRingMaxLds));
-  if (attr != hipSuccess) return attr;
-  if (lds > kDecodeRingMaxLds) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
-  {
-    ProfileScope ps(kDecode, stream);
-    hipLaunchKernelGGL((decode_ring_kernel<D, NS>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables, hw);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_reduce(a, stream, true);
-}
-
-// Stages per wave of the bf16 ring. PA_DECODE_RING=<n> forces n (for timing).
-int ring_stages(const AttnArgs& a) {
-  static const int forced = [] {
-    const char* e = std::getenv("PA_DECODE_RING");
-    return e ? std::atoi(e) : 0;
-  }();
-  if (forced == 1 || forced == 2 || (forced == 4 && a.D == 64)) return forced;
-  return 1;
+  if (e != hipSuccess || !with_reduce) return e;
+  return reduce_launch(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const AttnArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, bool with_reduce) {
+  const bool r = with_reduce;
   if (a.elem != Elem::BF16)
-    return a.D == 64 ? launch_staged<false, 64, false>(a, stream) : launch_staged<false, 128, false>(a, stream);
-  if (a.kv8) return a.D == 64 ? launch_staged<true, 64, true>(a, stream) : launch_staged<true, 128, true>(a, stream);
-  const int ns = ring_stages(a);
-  if (a.D == 64) {
-    if (ns == 4) return launch_ring<64, 4>(a, stream);
-    return ns == 1 ? launch_ring<64, 1>(a, stream) : launch_ring<64, 2>(a, stream);
-  }
-  return ns == 1 ? launch_ring<128, 1>(a, stream) : launch_ring<128, 2>(a, stream);
+    return a.D == 64 ? launch_staged<false, 64, false>(a, stream, r) : launch_staged<false, 128, false>(a, stream, r);
+  if (a.kv8) return a.D == 64 ? launch_staged<true, 64, true>(a, stream, r) : launch_staged<true, 128, true>(a, stream, r);
+  return a.D == 64 ? launch_staged<true, 64, false>(a, stream, r) : launch_staged<true, 128, false>(a, stream, r);
 }
+
+hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream) { return reduce_launch(a, stream); }
 
 }  // namespace pa

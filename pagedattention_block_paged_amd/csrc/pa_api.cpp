@@ -387,20 +387,30 @@ bool prefill_beside_decode(const pa::AttnArgs& a) {
 // disjoint rows of `out` and read only the inputs. For large mixed batches in
 // bf16 the prefill runs on a second stream, forked from and joined back into
 // `stream`, on a few CUs chosen by the plan kernel while the decode streams
-// on the rest; otherwise the two run one after the other on `stream`.
-pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream, bool allow_side = true) {
+// on the rest. Otherwise everything runs on `stream`: the plan (unless the
+// caller's KV write launch already made it), the decode, then the prefill
+// kernel, which first combines the decode's split-K partitions (one launch
+// fewer than a separate reduce).
+bool attention_beside(const pa::AttnArgs& a, bool allow_side) {
+  return allow_side && a.S > 0 && a.T > 0 && prefill_beside_decode(a);
+}
+
+pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream, bool allow_side = true, bool planned = false) {
   if (a.S == 0 || a.T == 0) return PA_OK;
-  SideStream* side = allow_side && prefill_beside_decode(a) ? side_stream_for(stream) : nullptr;
+  SideStream* side = attention_beside(a, allow_side) ? side_stream_for(stream) : nullptr;
   if (!side) {
-    PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
-    PA_TRY(hip_status(pa::launch_prefill(a, stream, false), "prefill launch"));
+    if (!planned) PA_TRY(hip_status(pa::launch_plan(a, stream, false), "plan launch"));
+    const bool fold = a.max_parts > 1 && pa::prefill_launches(a);
+    PA_TRY(hip_status(pa::launch_decode(a, stream, !fold), "decode launch"));
+    PA_TRY(hip_status(pa::launch_prefill(a, stream, false, fold), "prefill launch"));
     return PA_OK;
   }
   PA_TRY(hip_status(hipEventRecord(side->fork, stream), "fork event"));
   PA_TRY(hip_status(hipStreamWaitEvent(side->stream, side->fork, 0), "fork wait"));
-  // prefill first, so that its workgroups take their CUs before the decode's
-  PA_TRY(hip_status(pa::launch_prefill(a, side->stream, true), "prefill launch"));
-  PA_TRY(hip_status(pa::launch_decode(a, stream), "decode launch"));
+  // plan and prefill first, so that their workgroups take CUs before the decode's
+  PA_TRY(hip_status(pa::launch_plan(a, side->stream, true), "plan launch"));
+  PA_TRY(hip_status(pa::launch_prefill(a, side->stream, true, false), "prefill launch"));
+  PA_TRY(hip_status(pa::launch_decode(a, stream, true), "decode launch"));
   PA_TRY(hip_status(hipEventRecord(side->join, side->stream), "join event"));
   PA_TRY(hip_status(hipStreamWaitEvent(stream, side->join, 0), "join wait"));
   return PA_OK;
@@ -569,8 +579,11 @@ pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k
     if (w.T > 0) PA_TRY(check_write_contents(w, s));
     PA_TRY(check_attention_contents(a, s));
   }
-  if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
-  PA_TRY(run_attention(a, s, allow_side));
+  // Without a second stream the plan goes out in the KV write's launch.
+  const bool fused = w.T > 0 && a.S > 0 && !attention_beside(a, allow_side);
+  if (fused) PA_TRY(hip_status(pa::launch_write_plan(w, a, s), "kv write launch"));
+  else if (w.T > 0) PA_TRY(hip_status(pa::launch_kv_write(w, s), "kv write launch"));
+  PA_TRY(run_attention(a, s, allow_side, fused));
   return ok();
 }
 

@@ -102,7 +102,7 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB);
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB);
 
 // Optional per-kernel HIP-event timing (include/pa_profile.h).
-enum KernelId { kKvWrite = 0, kDecode = 1, kReduce = 2, kPlan = 3, kPrefill = 4 };
+enum KernelId { kKvWrite = 0, kDecode = 1, kReduce = 2, kPlan = 3, kPrefill = 4, kWritePlan = 5 };
 bool profiling();
 void profile_mark(int id, bool end, hipStream_t stream);
 struct ProfileScope {
@@ -126,11 +126,19 @@ pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k
                     void* workspace, size_t workspace_bytes, pa_stream stream, bool allow_side);
 
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
-// Decode kernel, then the partition reduce (decode.hip).
-hipError_t launch_decode(const AttnArgs& a, hipStream_t stream);
-// Plan kernel, then the chunked-prefill kernel (prefill.hip). `beside`: the
-// prefill runs concurrently with the decode kernel (another stream), on the
-// share of the CUs the plan kernel sets (bf16 only).
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside);
+// Decode kernel, then (with_reduce) the partition reduce (decode.hip).
+hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, bool with_reduce);
+// The partition reduce alone (decode.hip).
+hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream);
+// prefill.hip: the plan kernel (prefill tile list and queue, and the
+// prefill's share of the CUs when it runs `beside` the decode on another
+// stream); the plan and the KV write in one launch (when the prefill runs
+// after the decode); the chunked-prefill kernel, after a plan, which first
+// combines the decode's partitions when `fold_reduce` (it then runs after the
+// decode on the same stream); and whether a prefill launch has any workgroup.
+hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, bool beside);
+hipError_t launch_write_plan(const WriteArgs& w, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside, bool fold_reduce);
+bool prefill_launches(const AttnArgs& a);
 
 }  // namespace pa

@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "pa_internal.h"
+#include "step_parts.h"
 
 namespace pa {
 namespace {
@@ -99,7 +100,7 @@ constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
 // the decode kernel: enough CUs that the prefill work takes about half as
 // long as the decode work on the rest (all slots when there is no decode
 // work).
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const int32_t* ctx_lens,
+__device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
                                                     const int32_t* seq_lens, const int32_t* block_tables,
                                                     int64_t bt_row, int64_t S, int64_t T, int64_t MB,
                                                     int64_t G, int qtile, int64_t Hq, int64_t D,
@@ -230,6 +231,43 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* qsl, const in
     rec[2] = make_int4(id(0), id(1), id(2), id(3));
     rec[3] = make_int4(id(4), id(5), id(6), id(7));
   }
+}
+
+// The plan parameters a launch passes to plan_body.
+struct PlanArgs {
+  const int32_t* qsl;
+  const int32_t* ctx_lens;
+  const int32_t* seq_lens;
+  const int32_t* block_tables;
+  int64_t bt_row, S, T, MB, G;
+  int qtile;
+  int64_t Hq, D, kv_token_bytes;
+  int items_per_tile, slots, beside;
+  float flop_per_cu_us;
+  int wg_per_cu;
+  float ratio;
+  int32_t *tile_start, *tile_order, *counter;
+};
+
+__device__ inline void plan_with(const PlanArgs& p) {
+  plan_body(p.qsl, p.ctx_lens, p.seq_lens, p.block_tables, p.bt_row, p.S, p.T, p.MB, p.G, p.qtile, p.Hq, p.D,
+            p.kv_token_bytes, p.items_per_tile, p.slots, p.beside, p.flop_per_cu_us, p.wg_per_cu, p.ratio,
+            p.tile_start, p.tile_order, p.counter);
+}
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanArgs p) { plan_with(p); }
+
+// One launch for a step whose prefill runs after its decode: workgroup 0
+// plans (as plan_kernel), the others write the step's new K/V into the pool
+// (as the KV write kernels, 1024 lanes per workgroup). Nothing reads the
+// pool before the launch has ended, so the two need no ordering.
+__global__ __launch_bounds__(1024) void write_plan_kernel(WriteArgs w, int vec_per_head, int tpb, PlanArgs p) {
+  if (blockIdx.x == 0) {
+    plan_with(p);
+    return;
+  }
+  if (w.kv8) kv_write_fp8_tokens(w, vec_per_head, tpb, int64_t(blockIdx.x) - 1, 1024);
+  else kv_write_tokens(w, vec_per_head, tpb, int64_t(blockIdx.x) - 1, 1024);
 }
 
 // Which sequence and local tile a queue item names, with the sequence's
@@ -909,9 +947,16 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 // others exit at once and leave their CUs to the decode.
 template <int D, int HW, bool KV8>
 __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
-                                                                 int beside) {
+                                                                 int beside, int fold_reduce) {
   const int active = beside ? min(a.work_counter[1], static_cast<int>(gridDim.x)) : static_cast<int>(gridDim.x);
   if (static_cast<int>(blockIdx.x) >= active) return;
+  // After the decode on the same stream, the waves first combine the decode's
+  // split-K partitions (one (sequence, query head) per wave at a time).
+  if (fold_reduce) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t it = int64_t(blockIdx.x) * kPWaves + wave; it < a.S * a.Hq; it += int64_t(gridDim.x) * kPWaves)
+      reduce_partitions<true, D>(a, it, threadIdx.x & 63);
+  }
   // No static LDS: the dynamic array starts at address 0, so fragment
   // addresses are a per-lane offset plus an immediate.
   extern __shared__ uint4 lds[];
@@ -930,9 +975,16 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int HW, bool KV8>
-__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a, int beside) {
+__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a, int beside, int fold_reduce) {
   // beside the decode kernel only the plan kernel's share of workgroups take items
   if (beside && static_cast<int>(blockIdx.x) >= min(a.work_counter[1], static_cast<int>(gridDim.x))) return;
+  // After the decode on the same stream: first the decode's partition reduce
+  // (q and out are bf16 over an 8-bit pool, fp32 otherwise).
+  if (fold_reduce) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t it = int64_t(blockIdx.x) * kWaves + wv; it < a.S * a.Hq; it += int64_t(gridDim.x) * kWaves)
+      reduce_partitions<KV8, D>(a, it, threadIdx.x & 63);
+  }
   constexpr int KT = 32;        // keys per LDS stage
   constexpr int KROW = D + 4;   // floats per K tile row
   constexpr int VROW = KT + 4;  // floats per V^T tile row
@@ -1095,33 +1147,69 @@ int64_t prefill_slots(const AttnArgs& a) {
 }
 
 template <bool BF16, int D, int HW>
-hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, int64_t slots, bool beside) {
-  constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
-  ProfileScope ps(kPlan, stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, a.qsl, a.ctx_lens, a.seq_lens, a.block_tables,
-                     a.bt_row, a.S, a.T, a.MB, a.Hq / a.Hkv, QTB, a.Hq, a.D,
-                     2 * a.Hkv * a.D * (a.kv8 ? 1 : (a.elem == Elem::BF16 ? 2 : 4)),
-                     static_cast<int>(a.Hkv * (a.Hq / a.Hkv / HW)), static_cast<int>(slots), beside ? 1 : 0,
-                     BF16 ? kPrefillFlopPerCuUs : kPrefillF32FlopPerCuUs, BF16 ? 1 : kThreadsPerCuF32 / kThreads,
-                     BF16 ? 2.f : kBesideRatioF32,
-                     a.tile_start, a.tile_order, a.work_counter);
-  return hipGetLastError();
+PlanArgs plan_args(const AttnArgs& a, int64_t slots, bool beside) {
+  PlanArgs p{};
+  p.qsl = a.qsl;
+  p.ctx_lens = a.ctx_lens;
+  p.seq_lens = a.seq_lens;
+  p.block_tables = a.block_tables;
+  p.bt_row = a.bt_row;
+  p.S = a.S;
+  p.T = a.T;
+  p.MB = a.MB;
+  p.G = a.Hq / a.Hkv;
+  p.qtile = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
+  p.Hq = a.Hq;
+  p.D = a.D;
+  p.kv_token_bytes = 2 * a.Hkv * a.D * (a.kv8 ? 1 : (a.elem == Elem::BF16 ? 2 : 4));
+  p.items_per_tile = static_cast<int>(a.Hkv * (a.Hq / a.Hkv / HW));
+  p.slots = static_cast<int>(slots);
+  p.beside = beside ? 1 : 0;
+  p.flop_per_cu_us = BF16 ? kPrefillFlopPerCuUs : kPrefillF32FlopPerCuUs;
+  p.wg_per_cu = BF16 ? 1 : kThreadsPerCuF32 / kThreads;
+  p.ratio = BF16 ? 2.f : kBesideRatioF32;
+  p.tile_start = a.tile_start;
+  p.tile_order = a.tile_order;
+  p.counter = a.work_counter;
+  return p;
 }
 
+// What one call of the prefill launcher puts on the stream: the plan (alone,
+// or with the KV write `write` in one launch), then the prefill kernel
+// (folding in the decode's partition reduce when asked).
+struct Launch {
+  bool plan, prefill, beside, fold_reduce;
+  const WriteArgs* write;
+};
+
 template <bool BF16, int D, int HW, bool KV8 = false>
-hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
+hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, const Launch& l) {
   const int64_t grid = prefill_slots<BF16, D, HW>(a);
-  hipError_t e = launch_plan<BF16, D, HW>(a, stream, grid, beside);
-  if (e != hipSuccess || grid == 0) return e;
+  if (l.write) {
+    const WriteArgs& w = *l.write;
+    const int vec_per_head = static_cast<int>(w.kv8 ? w.D / 16 : w.D * w.es / 16);
+    const int vec_per_tok = 2 * static_cast<int>(w.Hkv) * vec_per_head;
+    const int tpb = vec_per_tok >= 1024 ? 1 : 1024 / vec_per_tok;
+    const int64_t blocks = 1 + (w.T + tpb - 1) / tpb;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    ProfileScope ps(kWritePlan, stream);
+    hipLaunchKernelGGL(write_plan_kernel, dim3(static_cast<unsigned>(blocks)), dim3(1024), 0, stream, w,
+                       vec_per_head, tpb, plan_args<BF16, D, HW>(a, grid, l.beside));
+  } else if (l.plan) {
+    ProfileScope ps(kPlan, stream);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, plan_args<BF16, D, HW>(a, grid, l.beside));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !l.prefill || grid == 0) return e;
   // Workgroups pull items from the queue until it is empty.
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {
       hipLaunchKernelGGL((prefill_bf16_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kPThreads),
-                         bf16_lds_bytes<D>(), stream, a, a.block_tables, beside ? 1 : 0);
+                         bf16_lds_bytes<D>(), stream, a, a.block_tables, l.beside ? 1 : 0, l.fold_reduce ? 1 : 0);
     } else {
       hipLaunchKernelGGL((prefill_f32_kernel<D, HW, KV8>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0,
-                         stream, a, beside ? 1 : 0);
+                         stream, a, l.beside ? 1 : 0, l.fold_reduce ? 1 : 0);
     }
   }
   return hipGetLastError();
@@ -1129,11 +1217,19 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, bool beside) {
 
 // KV8: an 8-bit pool, attended by the fp32-MFMA kernel (the f32 work layout).
 template <bool BF16, int D, bool KV8 = false>
-hipError_t launch_heads(const AttnArgs& a, hipStream_t stream, bool beside) {
+hipError_t launch_heads(const AttnArgs& a, hipStream_t stream, const Launch& l) {
   const int64_t G = a.Hq / a.Hkv;
-  if (G % 4 == 0) return launch_typed<BF16, D, 4, KV8>(a, stream, beside);
-  if (G % 2 == 0) return launch_typed<BF16, D, 2, KV8>(a, stream, beside);
-  return launch_typed<BF16, D, 1, KV8>(a, stream, beside);
+  if (G % 4 == 0) return launch_typed<BF16, D, 4, KV8>(a, stream, l);
+  if (G % 2 == 0) return launch_typed<BF16, D, 2, KV8>(a, stream, l);
+  return launch_typed<BF16, D, 1, KV8>(a, stream, l);
+}
+
+template <bool BF16, int D>
+int64_t slots_heads(const AttnArgs& a) {
+  const int64_t G = a.Hq / a.Hkv;
+  if (G % 4 == 0) return prefill_slots<BF16, D, 4>(a);
+  if (G % 2 == 0) return prefill_slots<BF16, D, 2>(a);
+  return prefill_slots<BF16, D, 1>(a);
 }
 
 template <int D, int HW, bool KV8 = false>
@@ -1145,7 +1241,9 @@ hipError_t allow_lds() {
 
 }  // namespace
 
-hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
+namespace {
+
+hipError_t run_launch(const AttnArgs& a, hipStream_t stream, const Launch& l) {
   static const hipError_t lds_ok = [] {
     hipError_t e = hipSuccess;
     for (hipError_t r : {allow_lds<64, 1>(), allow_lds<64, 2>(), allow_lds<64, 4>(), allow_lds<128, 1>(),
@@ -1157,11 +1255,31 @@ hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside) {
   if (lds_ok != hipSuccess) return lds_ok;
   // 8-bit pools: the bf16-MFMA kernel widens the codes at head size 128; the
   // fp32-MFMA kernel serves head size 64
-  if (a.kv8)
-    return a.D == 64 ? launch_heads<false, 64, true>(a, stream, beside) : launch_heads<true, 128, true>(a, stream, beside);
+  if (a.kv8) return a.D == 64 ? launch_heads<false, 64, true>(a, stream, l) : launch_heads<true, 128, true>(a, stream, l);
   const bool bf16 = a.elem == Elem::BF16;
-  if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, beside) : launch_heads<false, 64>(a, stream, beside);
-  return bf16 ? launch_heads<true, 128>(a, stream, beside) : launch_heads<false, 128>(a, stream, beside);
+  if (a.D == 64) return bf16 ? launch_heads<true, 64>(a, stream, l) : launch_heads<false, 64>(a, stream, l);
+  return bf16 ? launch_heads<true, 128>(a, stream, l) : launch_heads<false, 128>(a, stream, l);
+}
+
+}  // namespace
+
+hipError_t launch_plan(const AttnArgs& a, hipStream_t stream, bool beside) {
+  return run_launch(a, stream, Launch{true, false, beside, false, nullptr});
+}
+
+hipError_t launch_write_plan(const WriteArgs& w, const AttnArgs& a, hipStream_t stream) {
+  return run_launch(a, stream, Launch{false, false, false, false, &w});
+}
+
+hipError_t launch_prefill(const AttnArgs& a, hipStream_t stream, bool beside, bool fold_reduce) {
+  return run_launch(a, stream, Launch{false, true, beside, fold_reduce, nullptr});
+}
+
+bool prefill_launches(const AttnArgs& a) {
+  if (a.kv8) return (a.D == 64 ? slots_heads<false, 64>(a) : slots_heads<true, 128>(a)) > 0;
+  const bool bf16 = a.elem == Elem::BF16;
+  if (a.D == 64) return (bf16 ? slots_heads<true, 64>(a) : slots_heads<false, 64>(a)) > 0;
+  return (bf16 ? slots_heads<true, 128>(a) : slots_heads<false, 128>(a)) > 0;
 }
 
 }  // namespace pa
