@@ -52,6 +52,10 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) const uint4 lds_u4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
@@ -327,8 +331,6 @@ __device__ inline int64_t next_item(const AttnArgs& a, int* item_sh) {
 }
 
 // ---------------------------------------------------------------- bf16 ----
-typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct Bf16Tile {
@@ -915,21 +917,45 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     // waiting for the claim does not also wait for them.
     if (tid == 0) *item_sh = queue_base + claimed;  // queue items follow the first round
     if (wave_active) {
+      // The wave's 32 x D output tile goes out as whole rows: the lanes hold
+      // it transposed (lane (col, hh) has O^T[d = 32 dt + 8 q + 4 hh + r][token
+      // col], 8-byte pieces of 32 different rows per store), so it passes
+      // through LDS first. Row col's 16-byte chunk c = 4 dt + q sits at chunk
+      // position c ^ (col mod OCH): the writes (32 rows at one chunk) and the
+      // row reads (OCH lanes per row) are then one pass per 256 bytes.
+      // Its place: a half stage no wave reads any more. Every wave is past
+      // the last tile's barrier, so only the K stage of the last tile and
+      // the V stages of the last two tiles may still be read; no load is in
+      // flight. That leaves three K stages and two V stages, ten halves.
+      constexpr int OCH = D / 8;     // 16-byte chunks per output row
+      constexpr int RPI = 64 / OCH;  // rows per 16-byte-per-lane read
+      const int b = (nkt + 3) & 3;   // stage of the last tile
+      const uint32_t ot = wave < 6 ? static_cast<uint32_t>(((b + 1 + wave / 2) & 3) * TB + (wave & 1) * HALF)
+                                   : static_cast<uint32_t>(V0 + ((b + 1) & 3) * TB + (wave & 1) * HALF);
       const float l_tot = l_run + __shfl_xor(l_run, 32);
-      const int my_tok = i0 + col;
-      if (my_tok < n) {
-        const float inv = (KV8 ? a.v_scale : 1.f) / l_tot;
-        char* dst = a.out + (q0 + my_tok) * a.out_st + h * a.out_sh;
-        // lane holds O^T[d = 32 dt + 8 q + 4 hh + r][token col]
+      const float inv = (KV8 ? a.v_scale : 1.f) / l_tot;
+      // The lane index passes through an empty asm here, so that the
+      // addresses below are computed here and not kept in registers across
+      // the whole item loop.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int ocol = ln & 31, ohh = ln >> 5;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int d = 32 * dt + 8 * q + 4 * hh;
-            *reinterpret_cast<uint2*>(dst + 2 * d) =
-                make_uint2(pack_bf16(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv),
-                           pack_bf16(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv));
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int c = 4 * dt + q;
+          *reinterpret_cast<lds_u32x2*>(dma + ot + 16u * (ocol * OCH + (c ^ (ocol % OCH))) + 8u * ohh) =
+              u32x2{pack_bf16(o[dt][4 * q] * inv, o[dt][4 * q + 1] * inv),
+                    pack_bf16(o[dt][4 * q + 2] * inv, o[dt][4 * q + 3] * inv)};
+        }
+      const int c = ln % OCH;
+#pragma unroll
+      for (int i = 0; i < 32 / RPI; ++i) {
+        const int row = i * RPI + ln / OCH;
+        const u32x4 val = *reinterpret_cast<const lds_u32x4*>(dma + ot + 16u * (row * OCH + (c ^ (row % OCH))));
+        const int tok = i0 + row;
+        if (tok < n) *reinterpret_cast<u32x4*>(a.out + (q0 + tok) * a.out_st + h * a.out_sh + 16 * c) = val;
       }
     }
     // Hand the claimed item to every wave. The barrier waits only for the
