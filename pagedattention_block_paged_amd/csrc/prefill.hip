@@ -55,6 +55,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -587,12 +588,41 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     };
 
     bf16x8 qf[QS];  // Q^T (B operand): token col, d = 16 st + 8 hh .. +8
-    {
-      const char* qrow = a.q + (q0 + my_i) * a.q_st + h * a.q_sh + 16 * hh;
+    // Q comes in through LDS: loaded as whole rows (16 lanes per 256-byte
+    // row at D = 128), where loading the B operand directly would fetch 16
+    // bytes of each of 32 rows per instruction. Each wave stages its own 32
+    // rows in a half stage of K or V stages 2 and 3, which no tile uses before
+    // the item's first barrier; row r's 16-byte chunk c sits at chunk slot
+    // c ^ (r mod QCH), so that the fragment reads (32 rows at one chunk) are
+    // one pass per 256 bytes. Rows past the item's tokens repeat its last.
+    constexpr int QCH = D / 8;     // 16-byte chunks per Q row
+    constexpr int QRI = 64 / QCH;  // rows per 1 KiB load
+    const uint32_t qst = static_cast<uint32_t>((wave >> 1) < 2 ? (2 + (wave >> 1)) * TB : V0 + (wave >> 1) * TB) +
+                         (wave & 1) * HALF;
+    // (the lane index passes through an empty asm in both, so that their
+    // per-lane offsets are computed here, not kept across the item loop)
+    auto load_q = [&] {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int w0 = min(i0, n - 1);  // the wave's first (clamped) token
+      const char* qb = a.q + (q0 + w0) * a.q_st + h * a.q_sh;
+      const uint32_t qrec = static_cast<uint32_t>((n - 1 - w0) * a.q_st + 2 * D);
+#pragma unroll
+      for (int i = 0; i < 32 / QRI; ++i) {
+        const int r = i * QRI + ln / QCH;
+        const int tok = min(i0 + r, n - 1);
+        const int c = (ln % QCH) ^ (r % QCH);
+        load_lds16(qb, qrec, static_cast<uint32_t>((tok - w0) * a.q_st + 16 * c), dma + qst + 1024u * i);
+      }
+    };
+    auto read_q = [&] {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int qc = ln & 31, qh = ln >> 5;
 #pragma unroll
       for (int st = 0; st < QS; ++st)
-        qf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qrow + 32 * st));
-    }
+        qf[st] = *reinterpret_cast<const lds_bf16x8*>(rd + qst + 16u * (qc * QCH + ((2 * st + qh) ^ (qc % QCH))));
+    };
     // Pre-scaled by scale * log2(e) once the loads have landed (after the
     // first tiles' loads are out), so the scores come out in log2 units.
     // Rounding the scaled Q to bf16 perturbs each product term by at most
@@ -817,9 +847,12 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     using no = std::false_type;
 
     if (nkt > 0) {
-      // Prologue: tiles 0 and 1 in flight, wait for tile 0 (and the Q loads).
-      // An 8-bit pool's tile goes through registers: its codes are widened
-      // into the stage just before the barrier that publishes it.
+      // Prologue: Q, then tiles 0 and 1 in flight; wait for Q and tile 0,
+      // read this wave's Q fragments before the barrier (tile 2 may go into
+      // their stage after it). An 8-bit pool's tile goes through registers:
+      // its codes are widened into the stage just before the barrier that
+      // publishes it.
+      load_q();
       if constexpr (KV8) {
         first_id8(0);
         load_regs8(0, 0);
@@ -830,8 +863,8 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         } else {
           wait_vmem<0>();
         }
+        read_q();
         write_regs8(0, 0);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       } else {
         first_ids(0);
         load_tile(0, 0);
@@ -842,7 +875,9 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         } else {
           wait_vmem<0>();
         }
+        read_q();
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       raw_barrier();
       // Claim point for short items: after the last tile's loads went out.
       if (nkt <= 2) claim();
@@ -859,12 +894,6 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         if constexpr (KV8) load_id8(3);
         else load_ids(3);
       }
-      // The Q loads have landed (they were issued before tile 0). Passing the
-      // fragments through an empty asm tells the compiler so; otherwise it
-      // cannot prove it inside the tile loop and waits there on the vector-
-      // memory count, which would also wait for the tile loads in flight.
-#pragma unroll
-      for (int st = 0; st < QS; ++st) asm volatile("" : "+v"(qf[st]));
       scale_q();
       first_steps(0);                       // scores of slices 0 and 1, softmax 0
       // Tile u: wait for it (tile u + 1 may stay in flight), start loading
