@@ -431,11 +431,12 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
   // A partition is one decode workgroup's share of a sequence: 8 waves over
   // a group of KV heads. Take the largest partition (fewest partial results)
   // that still yields kMinDecodeWorkgroups on the longest sequences the
-  // block table allows (2 workgroups of 8 waves fit a CU; 256 CUs).
+  // block table allows (two per CU on 256 CUs).
   constexpr int64_t kMinDecodeWorkgroups = 512;
   const int64_t groups = S * (Hkv / decode_heads_per_workgroup(Hkv));
   const int64_t max_len = MB * kBlockTokens;
-  for (int64_t pt : {kMaxPartitionTokens, int64_t(1024), int64_t(512), int64_t(256), int64_t(128), int64_t(64)}) {
+  for (int64_t pt : {kMaxPartitionTokens, int64_t(2048), int64_t(1024), int64_t(512), int64_t(256), int64_t(128),
+                     int64_t(64)}) {
     const int64_t parts = (max_len + pt - 1) / pt;
     if (groups * parts >= kMinDecodeWorkgroups) return pt;
   }

@@ -21,8 +21,10 @@ constexpr int kWaves = 4;         // waves per workgroup (KV write, reduce, pref
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDecodeWaves = 8;   // waves per decode workgroup
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-// Largest split-K partition: a decode wave then walks at most 128 blocks.
-constexpr int64_t kMaxPartitionTokens = 2048;
+// Largest split-K partition (256 blocks). Batches with many sequences run
+// most of them as one partition (no partial results to write and combine);
+// the cap bounds how long the last workgroups of a launch can run.
+constexpr int64_t kMaxPartitionTokens = 4096;
 
 // The decode kernel's MFMA tiles have 16 columns: (new token, query head)
 // pairs of one KV head. A sequence whose n new tokens times G query heads fit
