@@ -477,6 +477,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
     }
   }
 
+  // With one wave per head (hw = 8) there is nothing to merge: the wave
+  // stores its own columns and ends, so that the waves which finish first
+  // free their slots for the next workgroup instead of waiting for the
+  // slowest. The values are those of the merge below for one wave (its
+  // weight is exp2(0) = 1).
+  if constexpr (BF16) {
+    if (wph == 1) {
+      float l_tot = l_run + __shfl_xor(l_run, 16);
+      l_tot += __shfl_xor(l_tot, 32);
+      if (n >= ncol) return;
+      const int64_t hq = int64_t(g) * G + n % G;
+      const int64_t t = q0 + n / G;  // the column's token
+      const float vs = KV8 ? a.v_scale : 1.f;
+      if (nparts == 1) {
+        const float inv = 1.f / l_tot;
+        char* dst = a.out + t * a.out_st + hq * a.out_sh;
+#pragma unroll
+        for (int u = 0; u < Sh::NACC; ++u) {
+          const int d = 16 * u + 4 * kg;
+          f32x4 v = o[u];
+          if constexpr (KV8) v *= vs;
+          *reinterpret_cast<uint2*>(dst + 2 * d) =
+              make_uint2(pack_bf16(v[0] * inv, v[1] * inv), pack_bf16(v[2] * inv, v[3] * inv));
+        }
+      } else {
+        const int64_t slot = (t * a.Hq + hq) * a.max_parts + p;
+#pragma unroll
+        for (int u = 0; u < Sh::NACC; ++u) {
+          f32x4 v = o[u];
+          if constexpr (KV8) v *= vs;
+          *reinterpret_cast<float4*>(a.ws_o + slot * D + 16 * u + 4 * kg) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (kg == 0) a.ws_ml[slot] = make_float2(m_run, l_tot);
+      }
+      return;
+    }
+  }
+
   // merge the waves of each head: LDS layout [wave][m: 16][l: 16][o: ncol * D]
   __syncthreads();  // K/V tiles are no longer in use
   const int wstride = 32 + ncol * D;
