@@ -560,6 +560,37 @@ def read_bandwidth(nbytes: int = 4 << 30, reps: int = 10) -> float:
     return nbytes / best / 1e9
 
 
+def read_probe_sizes(sizes, reps: int = 20) -> dict:
+    """The plain-read probe at the given byte counts (a batch's K/V bytes),
+    each timed read preceded by a 1 GiB read that evicts the buffer from the
+    caches, so that every byte comes from HBM as in a decode step. The HIP
+    event times include a few microseconds of launch overhead; a kernel trace
+    of the same run gives the probe kernel alone."""
+    import torch
+
+    import pagedattention_block_paged_amd as pa
+
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+    out = {}
+    for nbytes in sizes:
+        buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(reps):
+            pa.read_probe(flush)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pa.read_probe(buf)
+            e1.record()
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        times.sort()
+        out[str(nbytes)] = {"event_us_median": times[len(times) // 2], "event_us_min": times[0]}
+        del buf
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -577,6 +608,8 @@ def main():
                     help="cache eviction between timed steps (outside the step events)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing of the secondary workloads")
+    ap.add_argument("--read-probe-sizes", default="",
+                    help="comma-separated byte counts: also time the plain-read probe at these sizes")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
@@ -601,6 +634,10 @@ def main():
             secondary[r["workload"]] = r
     read_gbs = read_bandwidth()
     log(f"[bench] read probe: {read_gbs:.1f} GB/s (non-temporal read of 4 GiB, best of 10)")
+    probe_sizes = None
+    if args.read_probe_sizes:
+        probe_sizes = read_probe_sizes([int(x) for x in args.read_probe_sizes.split(",") if x])
+        log(f"[bench] read probe by size: {json.dumps(probe_sizes)}")
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -661,6 +698,7 @@ def main():
             "algorithmic_bytes": head.get("decode_kernel_bytes"),
             "read_probe_gbs": read_gbs,
             "frac_of_read_probe": (dec / read_gbs) if dec else None,
+            "read_probe_by_size": probe_sizes,
             "prefill": None if pre is None else {
                 "kernel": "prefill",
                 "bound": "mfma",
