@@ -232,7 +232,8 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         "dtype": wl.dtype,
         "kv_dtype": wl.pool_dtype,
         "pool_blocks": wl.num_blocks,
-        "partition_tokens": pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.max_blocks),
+        "partition_tokens": pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.head_size, wl.dtype, wl.max_blocks,
+                                                kv_fp8=wl.pool_dtype == "fp8"),
         "ms_per_step": ms,
         "ms_per_step_graph": graph_ms,
         "ms_per_step_median": per[len(per) // 2],

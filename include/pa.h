@@ -235,8 +235,17 @@ pa_status pa_step_noalloc(const pa_tensor* out, const pa_tensor* q, const pa_ten
 size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,
                                    int64_t num_kv_heads, int64_t head_size, int64_t max_blocks_per_seq);
 
-/* Tokens per split-K decode partition chosen for these extents (a multiple of 16). */
-int64_t pa_partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq);
+/*
+ * Tokens per split-K decode partition that pa_attention / pa_step choose for
+ * these extents and element types (a multiple of 16): the largest that still
+ * gives one round of decode workgroups on the longest sequences the block
+ * table allows, as many as the device's CUs hold at once. q_dtype is PA_F32
+ * or PA_BF16; cache_dtype is q_dtype, or PA_FP8_E4M3 with PA_BF16 queries.
+ * Without a device (the occupancy query fails) it assumes two workgroups per
+ * CU. Returns 0 for invalid arguments.
+ */
+int64_t pa_partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t head_size, int32_t q_dtype,
+                            int32_t cache_dtype, int64_t max_blocks_per_seq);
 
 /* Static description of a status code. */
 const char* pa_status_string(pa_status status);

@@ -87,7 +87,7 @@ def _load():
         getattr(lib, f).restype = ctypes.c_int
     lib.pa_attention_workspace_size.argtypes = [i64] * 6
     lib.pa_attention_workspace_size.restype = sz
-    lib.pa_partition_tokens.argtypes = [i64] * 3
+    lib.pa_partition_tokens.argtypes = [i64, i64, i64, ctypes.c_int32, ctypes.c_int32, i64]
     lib.pa_partition_tokens.restype = i64
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -163,8 +163,13 @@ def workspace_size(num_seqs: int, num_tokens: int, num_q_heads: int, num_kv_head
                                                max_blocks_per_seq))
 
 
-def partition_tokens(num_seqs: int, num_kv_heads: int, max_blocks_per_seq: int) -> int:
-    return int(lib.pa_partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq))
+def partition_tokens(num_seqs: int, num_kv_heads: int, head_size: int, dtype: str, max_blocks_per_seq: int,
+                     kv_fp8: bool = False) -> int:
+    """Decode partition size pa_attention / pa_step choose (pa_partition_tokens).
+    dtype: "bf16" or "f32" (queries and cache); kv_fp8: an 8-bit pool under bf16 queries."""
+    q = {"bf16": PA_BF16, "f32": PA_F32}[dtype]
+    return int(lib.pa_partition_tokens(num_seqs, num_kv_heads, head_size, q, PA_FP8_E4M3 if kv_fp8 else q,
+                                       max_blocks_per_seq))
 
 
 def new_workspace(q, key_cache, block_tables):

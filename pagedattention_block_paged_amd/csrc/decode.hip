@@ -572,20 +572,48 @@ hipError_t reduce_launch(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Dynamic LDS of a decode workgroup: the per-wave K/V tiles during the sweep,
+// then the merge area (up to 16 columns per wave).
+template <bool BF16, int D>
+constexpr size_t decode_lds_bytes() {
+  constexpr size_t merge = sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D);
+  constexpr size_t tiles = size_t(kDecodeWaves) * DecodeShape<BF16, D>::TILE_BYTES;
+  return merge > tiles ? merge : tiles;
+}
+
+// 16 query heads per KV head at D = 128 need 65 KB for the merge, past the
+// default dynamic-LDS limit.
 template <bool BF16, int D, bool KV8>
-hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce) {
-  using Sh = DecodeShape<BF16, D>;
-  const int hw = decode_heads_per_workgroup(a.Hkv);
-  const size_t merge = sizeof(float) * kDecodeWaves * (32 + kMaxDecodeColumns * D);  // up to 16 columns
-  const size_t tiles = size_t(kDecodeWaves) * Sh::TILE_BYTES;
-  const size_t lds = merge > tiles ? merge : tiles;
-  const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
-  // 16 query heads per KV head at D = 128 need 65 KB for the merge.
+hipError_t allow_decode_lds() {
   static const hipError_t attr =
       hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_kernel<BF16, D, 1, KV8>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kDecodeMaxLds));
+  return attr;
+}
+
+// Workgroups of this decode kernel one CU holds at once (its registers and
+// LDS, through the HIP occupancy query), or 0 when the query fails.
+template <bool BF16, int D, bool KV8>
+int decode_occupancy() {
+  static const int n = [] {
+    int blocks = 0;
+    if (allow_decode_lds<BF16, D, KV8>() != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void*>(&decode_kernel<BF16, D, 1, KV8>),
+                                                     kDecodeThreads, decode_lds_bytes<BF16, D>()) != hipSuccess)
+      return 0;
+    return blocks;
+  }();
+  return n;
+}
+
+template <bool BF16, int D, bool KV8>
+hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce) {
+  const int hw = decode_heads_per_workgroup(a.Hkv);
+  constexpr size_t lds = decode_lds_bytes<BF16, D>();
+  static_assert(lds <= kDecodeMaxLds, "decode LDS");
+  const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
+  const hipError_t attr = allow_decode_lds<BF16, D, KV8>();
   if (attr != hipSuccess) return attr;
-  if (lds > kDecodeMaxLds) return hipErrorInvalidValue;
   {
     ProfileScope ps(kDecode, stream);
     hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV8>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
@@ -607,5 +635,12 @@ hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, bool with_reduce
 }
 
 hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream) { return reduce_launch(a, stream); }
+
+int decode_workgroups_per_cu(Elem elem, bool kv8, int64_t D) {
+  if (D != 64 && D != 128) return 0;
+  if (elem != Elem::BF16) return D == 64 ? decode_occupancy<false, 64, false>() : decode_occupancy<false, 128, false>();
+  if (kv8) return D == 64 ? decode_occupancy<true, 64, true>() : decode_occupancy<true, 128, true>();
+  return D == 64 ? decode_occupancy<true, 64, false>() : decode_occupancy<true, 128, false>();
+}
 
 }  // namespace pa

@@ -308,7 +308,7 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   a->kv8 = fp8;
   a->k_scale = fp8 ? k_scale : 1.f;
   a->v_scale = fp8 ? v_scale : 1.f;
-  a->part_tokens = pa::partition_tokens(S, cs.Hkv, MB);
+  a->part_tokens = pa::partition_tokens(S, cs.Hkv, MB, pa::decode_workgroups_per_cu(a->elem, a->kv8, D));
   a->max_parts = (MB * pa::kBlockTokens + a->part_tokens - 1) / a->part_tokens;
   if (MB > (int64_t(1) << 26) || a->max_parts > 65535)
     return fail(PA_ERR_UNSUPPORTED, "block_tables has too many columns (%lld)", (long long)MB);
@@ -420,7 +420,7 @@ pa_status run_attention(const pa::AttnArgs& a, hipStream_t stream, bool allow_si
 
 namespace pa {
 
-int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
+int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB, int per_cu) {
   static const int64_t forced = [] {
     const char* e = std::getenv("PA_PARTITION_TOKENS");
     if (!e) return int64_t(0);
@@ -430,9 +430,12 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
   if (forced) return forced;
   // A partition is one decode workgroup's share of a sequence: 8 waves over
   // a group of KV heads. Take the largest partition (fewest partial results)
-  // that still yields kMinDecodeWorkgroups on the longest sequences the
-  // block table allows (two per CU on 256 CUs).
-  constexpr int64_t kMinDecodeWorkgroups = 512;
+  // that still yields one round of workgroups on the longest sequences the
+  // block table allows: 256 CUs times the workgroups a CU holds at once (one
+  // for the bf16 kernel at head size 128, two for the others). A second
+  // round of equally long workgroups only adds a tail. At most two per CU
+  // count (the workspace is sized for that), and two when unknown.
+  const int64_t kMinDecodeWorkgroups = 256 * (per_cu == 1 ? 1 : 2);
   const int64_t groups = S * (Hkv / decode_heads_per_workgroup(Hkv));
   const int64_t max_len = MB * kBlockTokens;
   for (int64_t pt : {kMaxPartitionTokens, int64_t(2048), int64_t(1024), int64_t(512), int64_t(256), int64_t(128),
@@ -446,7 +449,7 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB) {
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB) {
   auto align = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w{};
-  const int64_t pt = partition_tokens(S, Hkv, MB);
+  const int64_t pt = partition_tokens(S, Hkv, MB, 2);  // the most partitions any decode kernel takes
   const int64_t parts = (MB * kBlockTokens + pt - 1) / pt;
   w.tile_start_off = 0;
   w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
@@ -647,8 +650,16 @@ size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t
   return pa::workspace_layout(num_seqs, num_tokens, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq).total;
 }
 
-int64_t pa_partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t max_blocks_per_seq) {
-  return pa::partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq);
+int64_t pa_partition_tokens(int64_t num_seqs, int64_t num_kv_heads, int64_t head_size, int32_t q_dtype,
+                            int32_t cache_dtype, int64_t max_blocks_per_seq) {
+  const bool ok_types = (q_dtype == PA_F32 && cache_dtype == PA_F32) ||
+                        (q_dtype == PA_BF16 && (cache_dtype == PA_BF16 || cache_dtype == PA_FP8_E4M3));
+  if (num_seqs < 0 || num_kv_heads < 1 || max_blocks_per_seq < 1 || (head_size != 64 && head_size != 128) ||
+      !ok_types)
+    return 0;
+  const pa::Elem elem = q_dtype == PA_F32 ? pa::Elem::F32 : pa::Elem::BF16;
+  return pa::partition_tokens(num_seqs, num_kv_heads, max_blocks_per_seq,
+                              pa::decode_workgroups_per_cu(elem, cache_dtype == PA_FP8_E4M3, head_size));
 }
 
 const char* pa_status_string(pa_status s) {

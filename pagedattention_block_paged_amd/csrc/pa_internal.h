@@ -100,7 +100,9 @@ struct WorkspaceLayout {
   size_t tile_start_off, counter_off, order_off, ml_off, o_off, total;
 };
 
-int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB);
+// Tokens per split-K decode partition. per_cu: decode workgroups a CU holds at
+// once (decode_workgroups_per_cu; 0 if unknown); the workspace is sized for 2.
+int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB, int per_cu);
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB);
 
 // Optional per-kernel HIP-event timing (include/pa_profile.h).
@@ -130,6 +132,9 @@ pa_status step_impl(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k
 hipError_t launch_kv_write(const WriteArgs& a, hipStream_t stream);
 // Decode kernel, then (with_reduce) the partition reduce (decode.hip).
 hipError_t launch_decode(const AttnArgs& a, hipStream_t stream, bool with_reduce);
+// Workgroups of the decode kernel for these element types and head size that
+// one CU holds at once (HIP occupancy query); 0 when unknown.
+int decode_workgroups_per_cu(Elem elem, bool kv8, int64_t D);
 // The partition reduce alone (decode.hip).
 hipError_t launch_reduce(const AttnArgs& a, hipStream_t stream);
 // prefill.hip: the plan kernel (prefill tile list and queue, and the

@@ -104,12 +104,17 @@ def err():
 def test_workspace_size_and_partitions():
     assert pa.workspace_size(0, 0, 8, 2, 64, 8) > 0
     assert pa.workspace_size(4, 4, 8, 2, 64, 0) == 0
-    assert pa.partition_tokens(64, 4, 128) % 16 == 0
+    assert pa.partition_tokens(64, 4, 64, "bf16", 128) % 16 == 0
     # long contexts on few sequences split into more partitions than short ones
-    assert pa.partition_tokens(32, 8, 2048) >= pa.partition_tokens(64, 4, 128)
-    big = pa.workspace_size(32, 32, 64, 8, 128, 2048)
-    pt = pa.partition_tokens(32, 8, 2048)
-    assert big >= 32 * 64 * (2048 * 16 // pt) * 128 * 4
+    assert pa.partition_tokens(32, 8, 128, "bf16", 2048) >= pa.partition_tokens(64, 4, 64, "bf16", 128)
+    # the workspace holds the partials of every decode kernel's partitioning
+    for D, dt, fp8 in [(128, "bf16", False), (128, "bf16", True), (64, "bf16", False), (128, "f32", False)]:
+        big = pa.workspace_size(32, 32, 64, 8, D, 2048)
+        pt = pa.partition_tokens(32, 8, D, dt, 2048, kv_fp8=fp8)
+        assert big >= 32 * 64 * (2048 * 16 // pt) * D * 4
+    # invalid element types or head sizes
+    assert lib.pa_partition_tokens(4, 2, 96, 1, 1, 16) == 0
+    assert lib.pa_partition_tokens(4, 2, 128, 0, 4, 16) == 0
 
 
 @pytest.mark.parametrize("field,status", [

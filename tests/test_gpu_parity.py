@@ -259,10 +259,18 @@ def test_repeated_calls_are_deterministic(pa):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_partition_size_counts_resident_workgroups(pa):
+    """The partition size gives one round of decode workgroups: the bf16
+    kernel at head size 128 fits one workgroup per CU, the 8-bit-pool kernel
+    two (70B-batch extents: 32 sequences of up to 32768 tokens, 8 KV heads)."""
+    assert pa.partition_tokens(32, 8, 128, "bf16", 2048) == 4096
+    assert pa.partition_tokens(32, 8, 128, "bf16", 2048, kv_fp8=True) == 2048
+
+
 @pytest.mark.parametrize("delta", [-1, 0, 1, 17])
 def test_split_partition_boundaries(pa, delta):
     """Decode lengths around multiples of the partition size."""
-    pt = pa.partition_tokens(4, 2, 256)
+    pt = pa.partition_tokens(4, 2, 128, "bf16", 256)
     L = [pt + delta, 2 * pt + delta, 3 * pt + delta, 1]
     L = [max(1, x) for x in L]
     wl = W.build_workload("split", "bf16", 16, 2, 128, np.array(L) - 1, [1, 1, 1, 1], seed=40 + delta,
@@ -287,7 +295,7 @@ def test_short_queries_over_long_contexts(pa, Hq, Hkv, D, dtype):
     ctx = [4999, 2100, 64, 0] + [1500 + 700 * i for i in range(len(ns))] + [300]
     ql = [1, 1, 1, nmax] + ns + [nmax + 5]
     wl = W.build_workload(f"spec{Hq}x{Hkv}x{D}", dtype, Hq, Hkv, D, ctx, ql, seed=700 + Hq + D)
-    say(f"[spec] {dtype} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} q={ql} partition={pa.partition_tokens(wl.num_seqs, Hkv, wl.max_blocks)}")
+    say(f"[spec] {dtype} Hq={Hq} Hkv={Hkv} D={D} ctx={ctx} q={ql} partition={pa.partition_tokens(wl.num_seqs, Hkv, D, dtype, wl.max_blocks)}")
     c = device_case(wl)
     out = run_step(pa, wl, c)
     ref, _ = oracle.run_workload(wl)
