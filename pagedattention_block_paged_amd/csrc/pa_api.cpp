@@ -320,6 +320,7 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   a->tile_start = reinterpret_cast<int32_t*>(base + wl.tile_start_off);
   a->work_counter = reinterpret_cast<int32_t*>(base + wl.counter_off);
   a->tile_order = reinterpret_cast<int32_t*>(base + wl.order_off);
+  a->sched = reinterpret_cast<int32_t*>(base + wl.sched_off);
   a->ws_ml = reinterpret_cast<float2*>(base + wl.ml_off);
   a->ws_o = reinterpret_cast<float*>(base + wl.o_off);
   return PA_OK;
@@ -454,9 +455,12 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
   w.tile_start_off = 0;
   w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
   w.order_off = w.counter_off + 256;
-  w.ml_off = w.order_off + align(size_t(kMaxSortedTiles) * kTileRecord * sizeof(int32_t));
-  // split-K partials, one set per (new token, query head, partition) of the
-  // decode kernel's sequences
+  w.sched_off = w.order_off + align(size_t(kMaxSortedTiles) * kTileRecord * sizeof(int32_t));
+  w.ml_off = w.sched_off + align(size_t(2 * kMaxPrefillWorkgroups) * sizeof(int32_t));
+  // split-K partials, one set per (new token, query head, partition): the
+  // decode kernel's sequences use them for their partitions, and the bf16
+  // prefill for the key-range pieces of its split items (the rows of the
+  // prefill kernel's tokens, which the decode never touches)
   w.o_off = w.ml_off + align(size_t(T) * Hq * parts * sizeof(float2));
   w.total = w.o_off + align(size_t(T) * Hq * parts * D * sizeof(float));
   return w;

@@ -88,8 +88,14 @@ struct AttnArgs {
                           // they fit): sequence, tile, query start, query count, cached context, length,
                           // 2 unused, then the sequence's first 8 block-table entries
   int32_t* work_counter;  // [0] prefill work-queue head, zeroed by the plan kernel; [1] prefill workgroups that
-                          // run beside the decode kernel (set by the plan kernel)
+                          // run beside the decode kernel (set by the plan kernel); [2], [3] the bf16 prefill's
+                          // cost capacity per workgroup (int64, low word first)
+  int32_t* sched;         // [kMaxPrefillWorkgroups] first item of each bf16 prefill workgroup, then
+                          // [kMaxPrefillWorkgroups] merge counters of split items (both set by the plan kernel)
 };
+
+// The bf16 prefill launches at most one workgroup per CU.
+constexpr int kMaxPrefillWorkgroups = 256;
 
 // Up to this many prefill q-tiles are sorted by cost (longest first) before
 // the prefill kernel takes them from a queue; beyond it they go in order.
@@ -97,7 +103,7 @@ constexpr int kMaxSortedTiles = 4096;
 constexpr int kTileRecord = 16;  // int32 words per ranked-tile record
 
 struct WorkspaceLayout {
-  size_t tile_start_off, counter_off, order_off, ml_off, o_off, total;
+  size_t tile_start_off, counter_off, order_off, sched_off, ml_off, o_off, total;
 };
 
 // Tokens per split-K decode partition. per_cu: decode workgroups a CU holds at

@@ -8,11 +8,15 @@
 //
 // Design for gfx950 (the pages give no kernel design):
 //  - A plan kernel lists the q-tiles of every prefill sequence, sorts them by
-//    key count (longest first, when they fit in one workgroup's sort),
-//    records each rank's (sequence, tile) and resets a work-queue head, so
-//    the host never reads lengths. Workgroups take tiles from the queue until
-//    it is empty: longest-first greedy assignment keeps the 9x spread of
-//    chunk contexts from leaving a tail.
+//    key count (longest first, when they fit in one workgroup's sort) and
+//    records each rank's (sequence, tile), so the host never reads lengths.
+//    For the bf16 kernel it also splits the items' total cost into one equal
+//    share per workgroup (McNaughton's wrap-around rule over the ranked
+//    items): an item that straddles two shares is cut along its keys, each
+//    workgroup computes its piece, and the piece that finishes last combines
+//    the pieces' partial results. The 9x spread of chunk contexts then leaves
+//    no longest-item tail, and a few long items still fill every CU. The fp32
+//    kernel takes tiles from a work queue instead.
 //  - bf16: one workgroup of 8 waves per CU (two per SIMD) owns one (q-tile,
 //    KV head, group of HW query heads); wave w takes query head w % HW and
 //    32 tokens of sub-tile w / HW. The waves share K/V tiles of 64 keys.
@@ -55,6 +59,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) int lds_int;
 typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -66,6 +71,10 @@ constexpr float kRescaleBound = 256.0f;
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // parts: 32-bit data format, no index stride.
 constexpr int kBufferFlags = 0x00020000;
+// Cache policy of a buffer access that other XCDs' workgroups must see: sc1,
+// which the compiler also gives agent-scope atomic loads and stores (each XCD
+// has its own L2).
+constexpr int kCoherent = 16;
 constexpr int kWaveTokens = 32;
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -99,12 +108,32 @@ constexpr float kBesideRatioF32 = 1.0f;
 constexpr float kPrefillItemCuUs = 6.0f;
 constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
 
+// Static schedule of the bf16 prefill kernel. Costs are in quarters of a
+// 64-key tile: an item costs kItemFixedQ for its start and end plus 4 per
+// K/V tile it reads (measured on MI355X at head size 128: about 4.4 us per
+// item and 1.86 us per tile).
+constexpr int kPrefillKeyTile = 64;
+constexpr int64_t kItemFixedQ = 9;
+__device__ inline int64_t item_cost_q(int64_t key_tiles) { return kItemFixedQ + 4 * key_tiles; }
+// Workgroup b runs on XCD b mod 8, and each XCD has its own L2. The schedule
+// keeps the items of KV head g on the workgroups with b = g (mod nclass):
+// the token tiles of a chunk that read the same K/V then share one L2. Each
+// class splits its own items among its nwg / nclass workgroups (every rank
+// holds the same number of items of each class, so the classes' loads are
+// equal).
+__device__ inline int schedule_classes(int64_t Hkv, int nwg) {
+  const int c = Hkv % 8 == 0 ? 8 : Hkv % 4 == 0 ? 4 : Hkv % 2 == 0 ? 2 : 1;
+  return nwg % c == 0 ? c : 1;
+}
+
 // One block of 1024 threads: per-sequence tile counts, exclusive scan into
 // tile_start, cost-sorted tile order (if it fits), queue head reset, and the
 // number of prefill workgroups to run when the prefill shares the GPU with
 // the decode kernel: enough CUs that the prefill work takes about half as
 // long as the decode work on the rest (all slots when there is no decode
-// work).
+// work). With sorted tiles it also lays out the bf16 kernel's static
+// schedule: the cost prefix of every rank, each workgroup's equal share of
+// the total cost (its capacity) and the item in which each share starts.
 __device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
                                                     const int32_t* seq_lens, const int32_t* block_tables,
                                                     int64_t bt_row, int64_t S, int64_t T, int64_t MB,
@@ -112,8 +141,9 @@ __device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
                                                     int64_t kv_token_bytes, int items_per_tile, int slots,
                                                     int beside, float flop_per_cu_us, int wg_per_cu, float ratio,
                                                     int32_t* tile_start, int32_t* tile_order,
-                                                    int32_t* counter) {
+                                                    int32_t* counter, int32_t* sched) {
   __shared__ int32_t part[1024];
+  __shared__ int32_t n_active;
   __shared__ float red_dec[1024], red_pre[1024];
   __shared__ uint64_t keys[kMaxSortedTiles];
   __shared__ int32_t tile_seq[kMaxSortedTiles];  // sequence of each tile (sorted case)
@@ -196,7 +226,8 @@ __device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
     int active = 0;
     if (total > 0)
       active = (beside && dec > 0.f) ? static_cast<int>(ceilf(ratio * 256.f * pre / (pre + dec))) : slots;
-    counter[1] = min(max(active * wg_per_cu, total > 0 ? 1 : 0), slots);  // CUs -> workgroups
+    n_active = min(max(active * wg_per_cu, total > 0 ? 1 : 0), slots);  // CUs -> workgroups
+    counter[1] = n_active;
   }
   if (total > kMaxSortedTiles) return;  // uniform: tiles go in sequence order
   __syncthreads();
@@ -236,6 +267,85 @@ __device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
     rec[2] = make_int4(id(0), id(1), id(2), id(3));
     rec[3] = make_int4(id(4), id(5), id(6), id(7));
   }
+  if (sched == nullptr) return;
+  if (total == 0) {  // no prefill items: every workgroup's first item is past the end
+    for (int b = tid; b < kMaxPrefillWorkgroups; b += 1024) sched[b] = 0;
+    return;
+  }
+  // Cost prefix over the ranks (each rank stands for items_per_tile items of
+  // equal cost), kept in keys[] once every record is written.
+  __syncthreads();
+  int64_t* const pre = reinterpret_cast<int64_t*>(tile_seq);  // 1024 of its 2048 int64 slots
+  int64_t cr[kMaxSortedTiles / 1024];
+  int64_t csum = 0;
+#pragma unroll
+  for (int k = 0; k < kMaxSortedTiles / 1024; ++k) {
+    const int r = (kMaxSortedTiles / 1024) * tid + k;
+    const int64_t keys_r = r < total ? static_cast<int64_t>(keys[r] >> 32) : 0;
+    cr[k] = r < total ? item_cost_q((keys_r + kPrefillKeyTile - 1) / kPrefillKeyTile) * items_per_tile : 0;
+    csum += cr[k];
+  }
+  pre[tid] = csum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t v = tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    pre[tid] += v;
+    __syncthreads();
+  }
+  int64_t pos = pre[tid] - csum;
+  const int64_t p_total = pre[1023];
+#pragma unroll
+  for (int k = 0; k < kMaxSortedTiles / 1024; ++k) {
+    const int r = (kMaxSortedTiles / 1024) * tid + k;
+    if (r < total) {
+      keys[r] = static_cast<uint64_t>(pos);
+      int4* rec = reinterpret_cast<int4*>(tile_order + kTileRecord * r);
+      rec[1].z = static_cast<int32_t>(pos & 0xffffffff);
+      rec[1].w = static_cast<int32_t>(pos >> 32);
+    }
+    pos += cr[k];
+  }
+  __syncthreads();
+  // Equal shares within each class of items (schedule_classes): workgroup
+  // b = w nclass + x owns costs [w cap, (w + 1) cap) of class x, whose
+  // items in rank order have the cost prefix P_rank / nclass (+ the cost of
+  // the class's items before it in the rank); its first item (class-local
+  // index) is the one whose cost range holds w cap.
+  const int nwg = max(1, min(n_active, kMaxPrefillWorkgroups));
+  const int nclass = schedule_classes(Hq / G, nwg);
+  const int64_t cap = max(int64_t(1), (p_total + nwg - 1) / nwg);
+  // Cut items only when the longest one (rank 0) outlasts an equal share by
+  // more than a cut costs (a second item start, the partial result's write,
+  // count and combine: together about an eighth of a share here). Otherwise
+  // the longest-first queue balances the items whole.
+  const int64_t longest = (total > 1 ? static_cast<int64_t>(keys[1]) : p_total) / items_per_tile;
+  const bool cut = longest > cap + cap / 8;
+  if (tid == 0) {
+    counter[2] = cut ? static_cast<int32_t>(cap & 0xffffffff) : 0;
+    counter[3] = cut ? static_cast<int32_t>(cap >> 32) : 0;
+  }
+  if (!cut) return;
+  const int64_t per_class = items_per_tile / nclass;  // items of one class per rank
+  const int64_t class_items = int64_t(total) * per_class;
+  const int64_t class_total = p_total / nclass;
+  for (int b = tid; b < kMaxPrefillWorkgroups; b += 1024) {
+    sched[kMaxPrefillWorkgroups + b] = 0;  // merge counters
+    const int64_t at = int64_t(b / nclass) * cap;
+    int64_t first = class_items;
+    if (b < nwg && at < class_total) {
+      int lo = 0, hi = total - 1;  // last rank with class prefix <= at
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(keys[mid]) / nclass <= at) lo = mid; else hi = mid - 1;
+      }
+      const int64_t p0 = static_cast<int64_t>(keys[lo]) / nclass;
+      const int64_t p1 = (lo + 1 < total ? static_cast<int64_t>(keys[lo + 1]) : p_total) / nclass;
+      const int64_t per_item = (p1 - p0) / per_class;
+      first = int64_t(lo) * per_class + min(per_class - 1, (at - p0) / per_item);
+    }
+    sched[b] = static_cast<int32_t>(first);
+  }
 }
 
 // The plan parameters a launch passes to plan_body.
@@ -252,12 +362,13 @@ struct PlanArgs {
   int wg_per_cu;
   float ratio;
   int32_t *tile_start, *tile_order, *counter;
+  int32_t* sched;  // the bf16 kernel's static schedule; nullptr for the fp32 kernel (queue)
 };
 
 __device__ inline void plan_with(const PlanArgs& p) {
   plan_body(p.qsl, p.ctx_lens, p.seq_lens, p.block_tables, p.bt_row, p.S, p.T, p.MB, p.G, p.qtile, p.Hq, p.D,
             p.kv_token_bytes, p.items_per_tile, p.slots, p.beside, p.flop_per_cu_us, p.wg_per_cu, p.ratio,
-            p.tile_start, p.tile_order, p.counter);
+            p.tile_start, p.tile_order, p.counter, p.sched);
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(PlanArgs p) { plan_with(p); }
@@ -278,9 +389,10 @@ __global__ __launch_bounds__(1024) void write_plan_kernel(WriteArgs w, int vec_p
 // Which sequence and local tile a queue item names, with the sequence's
 // clamped query start, query count, cached context and length.
 struct TileRef {
-  int64_t s, lt, g, hg;
+  int64_t s, lt, g, hg, rank;
   int64_t q0, n, C, Lc;
-  bool ranked;        // from a plan record, which also holds
+  int64_t P;            // cost prefix of the rank (plan record; bf16 kernel only)
+  bool ranked;          // from a plan record, which also holds
   int4 ids_lo, ids_hi;  // the sequence's table entries 0 .. 3 and 4 .. 7
 };
 
@@ -290,6 +402,8 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
   const int64_t rest = item / a.Hkv;
   r.hg = rest % n_hg;
   const int64_t rank = rest / n_hg;
+  r.rank = rank;
+  r.P = 0;
   if (total_tiles <= kMaxSortedTiles) {  // the plan kernel wrote one record per rank
     const int4* rec = reinterpret_cast<const int4*>(a.tile_order + kTileRecord * rank);
     const int4 r0 = rec[0], r1 = rec[1], r2 = rec[2], r3 = rec[3];
@@ -299,6 +413,7 @@ __device__ inline TileRef locate(const AttnArgs& a, int64_t item, int n_hg, int6
     r.n = r0.w;
     r.C = r1.x;
     r.Lc = r1.y;
+    r.P = (static_cast<int64_t>(r1.w) << 32) | static_cast<uint32_t>(r1.z);
     r.ranked = true;
     r.ids_lo = r2;
     r.ids_hi = r3;
@@ -358,7 +473,9 @@ struct Bf16Tile {
 
 template <int D>
 constexpr size_t bf16_lds_bytes() {
-  return 2 * Bf16Tile<D>::STAGES * Bf16Tile<D>::TB + 16;  // K and V stages, then the queue slot
+  // K and V stages, then each wave's (max, sum) rows of a cut item's partial
+  // result, and the schedule's state
+  return 2 * Bf16Tile<D>::STAGES * Bf16Tile<D>::TB + kPWaves * 256 + 32;
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
@@ -392,19 +509,18 @@ __device__ __attribute__((always_inline)) inline void static_for(F&& f) {
   }
 }
 
-// One queue item after another. dma and rd are two views of the same LDS:
+// The workgroup's items one after another. dma and rd are two views of the same LDS:
 // the tile loads write through dma, the fragment reads go through rd. Between
 // two barriers a stage is either being loaded or being read, never both, so
 // the two kinds of access are independent; handing the compiler two distinct
 // restrict pointers lets it see that (otherwise it waits for every load in
 // flight before each LDS read).
-template <int D, int HW, bool KV8>
+template <int D, int HW, bool KV8, bool CUTS>
 __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const AttnArgs& a,
                                                                         const int32_t* __restrict__ bt_all,
                                                                         lds_char* __restrict__ dma,
                                                                         const lds_char* __restrict__ rd,
-                                                                        int* item_sh, int first_item,
-                                                                        int queue_base) {
+                                                                        int nwg) {
   using Tl = Bf16Tile<D>;
   constexpr int KT = Tl::KT, CPR = Tl::CPR, DPW = Tl::DPW;
   constexpr uint32_t TB = Tl::TB, HALF = Tl::HALF, V0 = Tl::V0;
@@ -474,14 +590,75 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
   const uint32_t dv8 = static_cast<uint32_t>((r8 % kBlockTokens) * a.vc_sr + 16 * c8);
   const uint32_t wk8 = 16u * Tl::chunk(r8, 2 * c8), wk8b = 16u * Tl::chunk(r8, 2 * c8 + 1);
 
-  // A workgroup's first item is its own index (items are ranked longest
-  // first, so this is the first round of a longest-first assignment); later
-  // items come from the queue. The next item is claimed while the current
-  // one's last key tile is in flight (thread 0 issues the atomic and keeps the
-  // result), so the claim's round trip overlaps compute; the queue order is
-  // still close to the order in which workgroups run out of work.
-  int64_t item = first_item;
-  while (item < n_items) {
+  // Two schedules, chosen by the plan kernel.
+  //  - Queue (the usual case): longest-first greedy assignment of whole items
+  //    (below).
+  //  - Cuts, when the longest item outlasts an equal share of the work (a few
+  //    long items, as in a long-context prefill): workgroup w of class x owns
+  //    the cost range [w cap, (w + 1) cap) of the class's items in rank order,
+  //    the items inside it whole and, of an item that a range boundary cuts,
+  //    the key tiles on its side of the cut (McNaughton's wrap-around rule). A
+  //    cut never lies past the position of the tile's first token, so both
+  //    pieces of an item see a key for every token: the first piece only keys
+  //    every token sees, the last piece the causal diagonal. Each piece of a
+  //    cut item writes its partial result (running maximum, weight sum and
+  //    unnormalised output per token and head) to the rows of its tokens in
+  //    the split-K workspace, at its piece index; the piece that counts in
+  //    last combines them in piece order, so the result does not depend on
+  //    which finishes first.
+  static_assert(KT == kPrefillKeyTile, "the plan's cost model counts 64-key tiles");
+  // No prefill items (the launch only combined the decode's partitions): the
+  // schedule may not have been written, so nothing of it is read.
+  if (n_items <= 0) return;
+  const int b = static_cast<int>(blockIdx.x);
+  const int64_t items_per_rank = a.Hkv * n_hg;
+  // Pieces per item: at most the workspace's partial slots per row, and none
+  // (no cut) when the 32-bit offsets of the partial stores could overflow.
+  const int max_pieces = 32 * a.Hq * a.max_parts * D * 4 < (int64_t(1) << 31) ? static_cast<int>(a.max_parts) : 1;
+  // Queue: workgroup b starts on item b (items are ranked longest first, so
+  // this is the first round of a longest-first assignment), later items come
+  // from the queue. The next item is claimed while the current one's last
+  // key tile is in flight (thread 0 issues the atomic and keeps the result),
+  // so the claim's round trip overlaps compute. Item b of the first round
+  // reads KV head b mod Hkv, and workgroup b runs on XCD b mod 8: the ranked
+  // token tiles of a chunk that read the same K/V start on one L2.
+  //
+  // The schedule's state lives in LDS, read where it is needed, so that none
+  // of it occupies scalar registers through the key loop: [0] merge count,
+  // [1] the loop's next index, [3..4] capacity, [5] pieces of the
+  // current item, [6] its piece index, [7] its merge counter.
+  lds_int* const st = reinterpret_cast<lds_int*>(dma + 2 * V0 + kPWaves * 256u);
+  const lds_int* const st_rd = reinterpret_cast<const lds_int*>(rd + 2 * V0 + kPWaves * 256u);
+  if (tid == 0) {
+    st[1] = CUTS ? a.sched[b] : b;  // class-local index of the schedule (cuts), or item index (queue)
+    if constexpr (CUTS) {  // the plan's capacity per workgroup
+      st[3] = a.work_counter[2];
+      st[4] = a.work_counter[3];
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  for (;;) {
+    const int64_t ci = __builtin_amdgcn_readfirstlane(st_rd[1]);
+    constexpr bool cuts = CUTS;
+    const int64_t cap = cuts ? max(int64_t(1), (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(st_rd[4])) << 32) |
+                                                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(st_rd[3])))
+                             : int64_t(1);
+    // This workgroup's class x (the KV heads g = x mod nclass) and its place
+    // w among the class's workgroups; with cuts, items are counted within
+    // the class.
+    const int nclass = schedule_classes(a.Hkv, nwg);
+    const int cx = b % nclass, w = b / nclass;
+    const int64_t heads_per_class = a.Hkv / nclass;
+    const int64_t per_class = items_per_rank / nclass;
+    if (cuts ? ci >= total_tiles * per_class : ci >= n_items) break;
+    const int64_t range_lo = int64_t(w) * cap, range_hi = range_lo + cap;
+    int64_t item = ci, k_in_rank = 0;
+    if (cuts) {  // class-local index -> item (rank, head group, KV head g = cx + nclass m)
+      const int64_t rank = ci / per_class;
+      k_in_rank = ci - rank * per_class;
+      const int64_t hg_c = k_in_rank / heads_per_class, m = k_in_rank - hg_c * heads_per_class;
+      item = rank * items_per_rank + hg_c * a.Hkv + cx + nclass * m;
+    }
     const TileRef tr = locate(a, item, n_hg, total_tiles);
     // Positions fit in 32 bits: keys are bounded by MB * 16 (checked on the host).
     const int64_t s = tr.s, g = tr.g;
@@ -489,22 +666,83 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     const int64_t q0 = tr.q0;
     const int n = static_cast<int>(tr.n);
     const int Lc = static_cast<int>(tr.Lc);
-    const int C = static_cast<int>(tr.C);
-    int claimed = 0;  // thread 0: the queue position of the next item
+    const int C_item = static_cast<int>(tr.C);
+    const int blk_last = min(n, (lt + 1) * QTB) - 1;                 // last token of the tile
+    const int kend_item = min(C_item + blk_last + 1, Lc);             // keys [0, kend_item) needed by the tile
+    const int nkt_item = (kend_item + KT - 1) / KT;
+    // This workgroup's piece of the item: key tiles [t_lo, t_hi), piece
+    // pidx of npieces.
+    int t_lo = 0, t_hi = nkt_item, pidx = 0, npieces = 1;
+    int64_t merge_slot = 0;  // first range boundary inside the item: its merge counter
+    int claimed = 0;  // queue: thread 0's claim of the next item
     auto claim = [&] {
-      if (tid == 0) claimed = atomicAdd(a.work_counter, 1);
+      if (!cuts && tid == 0) claimed = atomicAdd(a.work_counter, 1);
     };
+    if (cuts) {
+      const int64_t cost = item_cost_q(nkt_item);
+      const int64_t p_item = tr.P / nclass + k_in_rank * cost;
+      if (p_item >= range_hi) break;
+      if (p_item < range_lo || p_item + cost > range_hi) {
+        // The cut at range boundary x: the key tiles whose cost lies before x,
+        // at most up to the tile's first token position (and short of the
+        // last tile); 0 is no cut. Cuts grow with x; at most max_pieces - 1
+        // distinct ones are kept (one partial slot per piece), a boundary
+        // past them cuts nothing.
+        const int smax = max(0, min(nkt_item - 1, (C_item + lt * QTB) / KT));
+        auto cut_at = [&](int64_t x) {
+          return static_cast<int>(min(max((x - p_item - kItemFixedQ) >> 2, int64_t(0)), int64_t(smax)));
+        };
+        const int64_t j0 = p_item / cap + 1, j1 = (p_item + cost - 1) / cap;  // boundaries inside the item
+        merge_slot = j0 * nclass + cx;  // the workgroup whose share starts at the first of them
+        int prev = 0, ncut = 0;
+        for (int64_t j = j0; j <= j1; ++j) {
+          int c = cut_at(j * cap);
+          if (c > prev) {
+            if (ncut + 1 < max_pieces) {
+              ++ncut;
+              prev = c;
+            } else {
+              c = nkt_item;  // dropped
+            }
+          }
+          if (j == w) {
+            t_lo = c;
+            pidx = ncut;
+          }
+          if (j == w + 1) t_hi = c;
+          if (c == nkt_item) {
+            if (j <= w) t_lo = nkt_item;
+            break;
+          }
+        }
+        npieces = ncut + 1;
+      }
+    }
+    if (cuts && t_lo >= t_hi) {  // this workgroup has no piece of the item
+      asm volatile("s_barrier" ::: "memory");  // every wave has read the index
+      if (tid == 0) st[1] = static_cast<int>(ci + 1);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      continue;
+    }
+    if (CUTS && tid == 0) {
+      st[5] = npieces;
+      st[6] = pidx;
+      st[7] = static_cast<int>(merge_slot);
+    }
+    // The piece as an item of its own: keys shifted down by k0, the block
+    // table advanced by the tiles before it.
+    const int k0 = KT * t_lo;
+    const int C = C_item - k0;
+    const int kend = (t_hi == nkt_item ? kend_item : KT * t_hi) - k0;  // keys [0, kend) of the piece
+    const int nkt = t_hi - t_lo;
     const int64_t h = g * G + hg * HW + hw;
     const int i0 = lt * QTB + tw * kWaveTokens;  // first token of this wave
     const bool wave_active = i0 < n;
-    const int blk_last = min(n, (lt + 1) * QTB) - 1;  // last token of the tile
-    const int kend = min(C + blk_last + 1, Lc);       // keys [0, kend) needed by the tile
-    const int wave_first = C + min(i0, n - 1);        // smallest position among the wave's lanes
-    const int my_i = min(i0 + col, n - 1);            // clamped token of this lane
-    const int my_pos = C + my_i;                      // last key this lane sees
-    const int nkt = (kend + KT - 1) / KT;
+    const int wave_first = C + min(i0, n - 1);  // smallest position among the wave's lanes
+    const int my_i = min(i0 + col, n - 1);      // clamped token of this lane
+    const int my_pos = C + my_i;                // last key this lane sees
 
-    const int32_t* bt = bt_all + s * a.bt_row;
+    const int32_t* bt = bt_all + s * a.bt_row + (KT / kBlockTokens) * t_lo;
     const char* kc = a.kc + g * a.kc_sh;
     const char* vc = a.vc + g * a.vc_sh;
     const int last_blk = (kend - 1) / kBlockTokens;
@@ -520,8 +758,9 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     // Tiles 0 and 1 (blocks 0 .. 7) take their ids from the item's plan
     // record when it has one (read together with the item, picked by register
     // selects), not from the table: no round trip before the first loads.
+    const bool rec_ids = tr.ranked && t_lo == 0;  // the plan record holds the piece's first block ids
     auto first_ids = [&](int t) {
-      if (!tr.ranked) return load_ids(t);
+      if (!rec_ids) return load_ids(t);
 #pragma unroll
       for (int i = 0; i < DPW; ++i) {
         const int j = min(t * (KT / kBlockTokens) + blk_of(i), last_blk);
@@ -536,7 +775,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     int32_t id8 = 0;
     auto load_id8 = [&](int t) { id8 = bt[min(t * (KT / kBlockTokens) + wave / 2, last_blk)]; };
     auto first_id8 = [&](int t) {
-      if (!tr.ranked) return load_id8(t);
+      if (!rec_ids) return load_id8(t);
       const int j = min(t * (KT / kBlockTokens) + wave / 2, last_blk);
       const int4 q = j < 4 ? tr.ids_lo : tr.ids_hi;
       const int jj = j & 3;
@@ -907,7 +1146,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         // flight through the last tile.
         if (u + 1 < nkt)
           wait_vmem<KV8 ? 2 : 2 * DPW>();
-        else if (wave == 0)
+        else if (wave == 0 && !cuts)
           wait_vmem<1>();
         else
           wait_vmem<0>();
@@ -943,9 +1182,157 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
 
     if (nkt <= 0) claim();
     // The claimed item goes to LDS before this item's output stores, so that
-    // waiting for the claim does not also wait for them.
-    if (tid == 0) *item_sh = queue_base + claimed;  // queue items follow the first round
-    if (wave_active) {
+    // waiting for the claim does not also wait for them (queue items follow
+    // the first round).
+    if (tid == 0) st[1] = cuts ? st[1] + 1 : nwg + claimed;
+    // A cut item: this piece's partial result goes to the workspace, and the
+    // piece that counts in last combines every piece's.
+    const int npieces_e = CUTS ? __builtin_amdgcn_readfirstlane(st_rd[5]) : 1;
+    bool merge = false;
+    if (npieces_e > 1) {
+      const int npieces = npieces_e, pidx = __builtin_amdgcn_readfirstlane(st_rd[6]);
+      const int64_t merge_slot = __builtin_amdgcn_readfirstlane(st_rd[7]);
+      const int64_t row_bytes = a.Hq * a.max_parts * D * 4;  // workspace stride between tokens
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the stages
+      // The wave's unnormalised 32 x D output, fp32, as rows in LDS (one
+      // stage-sized region per wave): lane (col, hh) holds 16-byte chunk
+      // 8 dt + 2 q + hh of row col, at chunk position c ^ (row mod FCH); the
+      // row's running maximum and weight sum go to a small area after the
+      // stages.
+      constexpr int FCH = D / 4;       // 16-byte chunks per fp32 row
+      constexpr int RPR = 64 / FCH;    // rows per 16-byte-per-lane access
+      const uint32_t prow = static_cast<uint32_t>(wave) * TB;
+      const uint32_t pml = 2 * V0 + static_cast<uint32_t>(wave) * 256u;
+      {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int pc = ln & 31, ph = ln >> 5;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = 8 * dt + 2 * q + ph;
+            *reinterpret_cast<lds_u32x4*>(dma + prow + 16u * (pc * FCH + (c ^ (pc % FCH)))) =
+                u32x4{__float_as_uint(o[dt][4 * q]), __float_as_uint(o[dt][4 * q + 1]),
+                      __float_as_uint(o[dt][4 * q + 2]), __float_as_uint(o[dt][4 * q + 3])};
+          }
+        const float l_tot = l_run + __shfl_xor(l_run, 32);
+        if (ph == 0) *reinterpret_cast<lds_u32x2*>(dma + pml + 8u * pc) = u32x2{__float_as_uint(-negm[0]), __float_as_uint(l_tot)};
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // Rows to the workspace at this piece's index (cache-coherent stores:
+      // the combining workgroup may run on another XCD).
+      // The wave's rows: token q0 + i0 + r, head h; offsets from its first
+      // row fit 32 bits (max_pieces is 1 otherwise).
+      const int64_t row0 = (q0 + i0) * a.Hq + h;
+      const uint32_t ml_stride = static_cast<uint32_t>(a.Hq * a.max_parts * 8);  // between tokens
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char*>(a.ws_o + row0 * a.max_parts * D), 0, 0x7fffffff, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<char*>(a.ws_ml + row0 * a.max_parts), 0, 0x7fffffff, kBufferFlags);
+      if (wave_active) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int c = ln % FCH;
+#pragma unroll
+        for (int i = 0; i < 32 / RPR; ++i) {
+          const int r = i * RPR + ln / FCH;
+          const u32x4 v = *reinterpret_cast<const lds_u32x4*>(rd + prow + 16u * (r * FCH + (c ^ (r % FCH))));
+          if (i0 + r < n)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, ors, static_cast<uint32_t>(r * row_bytes + (pidx * D + 4 * c) * 4), 0, kCoherent);
+        }
+        if (ln < 32 && i0 + ln < n) {
+          const u32x2 v = *reinterpret_cast<const lds_u32x2*>(rd + pml + 8u * ln);
+          __builtin_amdgcn_raw_buffer_store_b64(v, mrs, static_cast<uint32_t>(ln) * ml_stride + 8u * pidx, 0, kCoherent);
+        }
+      }
+      // Count this piece in once every wave's stores have completed.
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      if (tid == 0)
+        st[0] = __hip_atomic_fetch_add(a.sched + kMaxPrefillWorkgroups + merge_slot, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      merge = __builtin_amdgcn_readfirstlane(st_rd[0]) == npieces - 1;
+      if (merge && wave_active) {
+        // Combine the pieces in piece order (online: rescale the running sum
+        // to each new maximum), this one's rows from LDS, the others' from the
+        // workspace with coherent loads, issued for four passes over the
+        // wave's rows at a time.
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int c = ln % FCH;
+        const float vs = KV8 ? a.v_scale : 1.f;
+        constexpr int NP = 4;  // passes per group
+        static_assert((32 / RPR) % NP == 0, "whole groups of passes");
+#pragma unroll 1
+        for (int half = 0; half < 32 / RPR / NP; ++half) {
+          float M[NP], L[NP], acc[NP][4];
+          uint32_t o_off[NP], m_off[NP];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            // rows past the item's tokens read the wave's last row instead
+            // (their results are not stored)
+            const int rr = min((half * NP + i) * RPR + ln / FCH, n - 1 - i0);
+            o_off[i] = static_cast<uint32_t>(rr * row_bytes + 16 * c);
+            m_off[i] = static_cast<uint32_t>(rr) * ml_stride;
+          }
+#pragma unroll 1
+          for (int p = 0; p < npieces; ++p) {
+            float mp[NP], lp[NP], op[NP][4];
+            if (p == pidx) {
+#pragma unroll
+              for (int i = 0; i < NP; ++i) {
+                const int r = (half * NP + i) * RPR + ln / FCH;
+                const u32x2 ml = *reinterpret_cast<const lds_u32x2*>(rd + pml + 8u * r);
+                const u32x4 o4 = *reinterpret_cast<const lds_u32x4*>(rd + prow + 16u * (r * FCH + (c ^ (r % FCH))));
+                mp[i] = __uint_as_float(ml.x);
+                lp[i] = __uint_as_float(ml.y);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) op[i][e] = __uint_as_float(o4[e]);
+              }
+            } else {
+#pragma unroll
+              for (int i = 0; i < NP; ++i) {
+                const float2 ml = __builtin_bit_cast(
+                    float2, __builtin_amdgcn_raw_buffer_load_b64(mrs, m_off[i] + 8u * p, 0, kCoherent));
+                const u32x4 o4 =
+                    __builtin_amdgcn_raw_buffer_load_b128(ors, o_off[i] + static_cast<uint32_t>(p * D * 4), 0, kCoherent);
+                mp[i] = ml.x;
+                lp[i] = ml.y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) op[i][e] = __uint_as_float(o4[e]);
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+              if (p == 0) {
+                M[i] = mp[i];
+                L[i] = lp[i];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][e] = op[i][e];
+              } else {
+                const float m_new = fmaxf(M[i], mp[i]);
+                const float wa = fast_exp2(M[i] - m_new), wb = fast_exp2(mp[i] - m_new);
+                M[i] = m_new;
+                L[i] = L[i] * wa + lp[i] * wb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][e] = acc[i][e] * wa + op[i][e] * wb;
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const int r = (half * NP + i) * RPR + ln / FCH;
+            const float inv = vs / L[i];
+            if (i0 + r < n)
+              *reinterpret_cast<u32x2*>(a.out + (q0 + i0 + r) * a.out_st + h * a.out_sh + 8 * c) =
+                  u32x2{pack_bf16(acc[i][0] * inv, acc[i][1] * inv), pack_bf16(acc[i][2] * inv, acc[i][3] * inv)};
+          }
+        }
+      }
+    }
+    if (npieces_e == 1 && wave_active) {
       // The wave's 32 x D output tile goes out as whole rows: the lanes hold
       // it transposed (lane (col, hh) has O^T[d = 32 dt + 8 q + 4 hh + r][token
       // col], 8-byte pieces of 32 different rows per store), so it passes
@@ -958,9 +1345,9 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
       // flight. That leaves three K stages and two V stages, ten halves.
       constexpr int OCH = D / 8;     // 16-byte chunks per output row
       constexpr int RPI = 64 / OCH;  // rows per 16-byte-per-lane read
-      const int b = (nkt + 3) & 3;   // stage of the last tile
-      const uint32_t ot = wave < 6 ? static_cast<uint32_t>(((b + 1 + wave / 2) & 3) * TB + (wave & 1) * HALF)
-                                   : static_cast<uint32_t>(V0 + ((b + 1) & 3) * TB + (wave & 1) * HALF);
+      const int ls = (nkt + 3) & 3;  // stage of the last tile
+      const uint32_t ot = wave < 6 ? static_cast<uint32_t>(((ls + 1 + wave / 2) & 3) * TB + (wave & 1) * HALF)
+                                   : static_cast<uint32_t>(V0 + ((ls + 1) & 3) * TB + (wave & 1) * HALF);
       const float l_tot = l_run + __shfl_xor(l_run, 32);
       const float inv = (KV8 ? a.v_scale : 1.f) / l_tot;
       // The lane index passes through an empty asm here, so that the
@@ -987,11 +1374,11 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         if (tok < n) *reinterpret_cast<u32x4*>(a.out + (q0 + tok) * a.out_st + h * a.out_sh + 16 * c) = val;
       }
     }
-    // Hand the claimed item to every wave. The barrier waits only for the
-    // LDS write, not for this item's output stores. Every wave reads the slot
-    // before its next barrier, and the slot is next written after one.
+    // The next item reuses the stages: every wave's LDS accesses must be
+    // done, and the claimed item is in LDS (the barrier does not wait for
+    // this item's output stores). Every wave reads the slot before its next
+    // barrier, and the slot is next written after one.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    item = __builtin_amdgcn_readfirstlane(*item_sh);
   }
 }
 
@@ -1015,12 +1402,20 @@ __global__ __launch_bounds__(kPThreads) void prefill_bf16_kernel(AttnArgs a, con
   // No static LDS: the dynamic array starts at address 0, so fragment
   // addresses are a per-lane offset plus an immediate.
   extern __shared__ uint4 lds[];
-  int* item_sh = reinterpret_cast<int*>(reinterpret_cast<char*>(lds) + 2 * Bf16Tile<D>::STAGES * Bf16Tile<D>::TB);
   // The load view is offset by an opaque zero so that the two views are
   // distinct values (identical arguments would defeat the restrict hint).
   uint32_t zero = 0;
   asm volatile("" : "+s"(zero));
-  prefill_bf16_items<D, HW, KV8>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, item_sh, blockIdx.x, active);
+  // The plan's schedule: cuts when it wrote a capacity (ranked items only),
+  // else the queue. Each is its own instance of the item loop, so that the
+  // queue's key loop carries none of the cuts' state.
+  const int64_t total_tiles = a.tile_start[a.S];
+  const bool cut_mode = total_tiles > 0 && total_tiles <= kMaxSortedTiles &&
+                        (a.work_counter[2] != 0 || a.work_counter[3] != 0);
+  if (cut_mode)
+    prefill_bf16_items<D, HW, KV8, true>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, active);
+  else
+    prefill_bf16_items<D, HW, KV8, false>(a, bt_all, (lds_char*)lds + zero, (const lds_char*)lds, active);
 }
 
 // ---------------------------------------------------------------- fp32 ----
@@ -1226,6 +1621,7 @@ PlanArgs plan_args(const AttnArgs& a, int64_t slots, bool beside) {
   p.tile_start = a.tile_start;
   p.tile_order = a.tile_order;
   p.counter = a.work_counter;
+  p.sched = BF16 ? a.sched : nullptr;
   return p;
 }
 
@@ -1256,7 +1652,8 @@ hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, const Launch& l) 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !l.prefill || grid == 0) return e;
-  // Workgroups pull items from the queue until it is empty.
+  // bf16: each workgroup takes its share of the static schedule; fp32:
+  // workgroups pull items from the queue until it is empty.
   {
     ProfileScope ps(kPrefill, stream);
     if constexpr (BF16) {

@@ -156,3 +156,13 @@ def test_fp8_heavier_tailed_context_within_absolute_bounds(pa):
         f"per-row max / rms {rel:.4g}")
     assert np.isfinite(out).all()
     assert err.max() <= 2e-2 and err.mean() <= 1e-2
+
+
+def test_fp8_prefill_items_cut_along_keys(pa):
+    """A few long prefill items over an 8-bit pool: the static schedule cuts
+    each into many pieces, combined by the piece that finishes last."""
+    wl = W.with_fp8_pool(W.build_workload("fp8cut", "bf16", 32, 8, 128, [30000, 700], [128, 1], seed=6064), 0.4, 0.3)
+    say(f"[fp8 cut] {wl.name}")
+    out = run_fp8_step(pa, wl)
+    ref, _ = oracle.run_workload(wl)
+    assert_within(out, ref, "bf16", wl.name)

@@ -360,3 +360,41 @@ def test_prefill_tiles_past_the_sorted_plan(pa, dtype):
     pool, _, _, _ = host_inputs(wl)
     ref, _ = oracle.run_workload(wl, pool=pool)
     say(f"[tiles] {assert_within(to_f64(out), ref, dtype, 'unsorted tiles')}")
+
+
+def cut_cases():
+    """Batches whose prefill items the static schedule cuts along their keys:
+    a few long items on 256 workgroups (each item in many pieces), the same at
+    head size 64, and one chunk next to 600 decodes, where the decode's
+    partition size leaves two partial slots per row (one cut per item: the
+    later range boundaries inside an item cut nothing)."""
+    rs = np.random.default_rng(6060)
+    return [
+        W.build_workload("cut_many", "bf16", 32, 8, 128, [30000, 500], [128, 1], seed=6061),
+        W.build_workload("cut_many_d64", "bf16", 16, 4, 64, [20000, 3, 9000], [200, 1, 70], seed=6062),
+        W.build_workload("cut_two_slots", "bf16", 32, 8, 128, list(rs.integers(1, 100, size=600)) + [8000],
+                         [1] * 600 + [64], seed=6063),
+    ]
+
+
+@pytest.mark.parametrize("idx", range(3))
+def test_prefill_items_cut_along_keys(pa, idx):
+    """Every row against the oracle, and bit-identical on a second call: the
+    pieces of a cut item are combined in piece order whichever finishes last."""
+    wl = cut_cases()[idx]
+    G = wl.num_q_heads // wl.num_kv_heads
+    pt = pa.partition_tokens(wl.num_seqs, wl.num_kv_heads, wl.head_size, "bf16", wl.max_blocks)
+    slots = -(-wl.max_blocks * 16 // pt)
+    say(f"[cut {idx}] {wl.name}: Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} D={wl.head_size} S={wl.num_seqs} "
+        f"partial slots per row {slots}")
+    assert any(n * G > 16 for n in wl.query_lens), "the case needs prefill items"
+    if idx == 2:
+        assert slots == 2, "the case must leave two partial slots per row"
+    c = device_case(wl)
+    ws = pa.new_workspace(c["q"], c["pool"][:, 0], c["block_tables"])
+    out = run_step(pa, wl, c, workspace=ws).clone()
+    out2 = run_step(pa, wl, c, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.run_workload(wl)
+    say(f"[cut {idx}] {assert_within(to_f64(out), ref, 'bf16', wl.name)}")
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
