@@ -21,8 +21,10 @@ beside the decode kernel on a few CUs, so the prefill roofline is timed on the
 same chunks run alone. `secondary` holds the other workloads -- the tiny fp32
 decode, the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode, the
 shared-prefix decode, a speculative-decode verification batch (4 new tokens
-per sequence over long contexts) and the 70B decode and 8B mixed step over an
-8-bit pool -- each over 20 timed steps (mean, median, min) and also timed as
+per sequence over long contexts), the 70B decode and 8B mixed step over an
+8-bit pool, and the last 512-token chunk of a 32,512-token prompt (64 long
+prefill items, which the prefill's schedule cuts along their keys to fill
+every CU) -- each over 20 timed steps (mean, median, min) and also timed as
 one HIP-graph replay per step (`ms_per_step_graph`). The decode's fraction is
 quoted against the 8 TB/s spec and against a non-temporal read probe run on
 the same GPU. `cpu_baseline` times the oracle on the host cores.
@@ -597,8 +599,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-8)")
-    ap.add_argument("--secondary", default="1,2,4,5,6,7,8", help="other workloads to measure, or 'none'")
+    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-9)")
+    ap.add_argument("--secondary", default="1,2,4,5,6,7,8,9", help="other workloads to measure, or 'none'")
     ap.add_argument("--secondary-steps", type=int, default=20)
     ap.add_argument("--secondary-warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -1585,15 +1585,19 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(AttnArgs a, int b
 }
 
 // Prefill workgroups to launch: enough to fill every CU (bf16: one 8-wave
-// workgroup per CU; fp32: four 4-wave), at most an upper bound on the items
-// that needs no lengths (every prefill sequence has more than 16 / G tokens).
+// workgroup per CU; fp32: four 4-wave), none when an upper bound on the items
+// that needs no lengths (every prefill sequence has more than 16 / G tokens)
+// is zero. The fp32 kernel launches at most that many; the bf16 kernel always
+// fills the CUs, because its schedule may cut a few long items into pieces
+// for all of them (with the queue, workgroups past the last item exit).
 template <bool BF16, int D, int HW>
 int64_t prefill_slots(const AttnArgs& a) {
   constexpr int QTB = BF16 ? bf16_tile_tokens(HW) : tile_tokens(HW);
   const int64_t G = a.Hq / a.Hkv;
   const int64_t tiles_ub = a.T / QTB + std::min<int64_t>(a.S, a.T / (kMaxDecodeColumns / G + 1));
   const int64_t items_ub = tiles_ub * a.Hkv * (G / HW);
-  return std::min<int64_t>(items_ub, BF16 ? 256 : 1024);
+  if (items_ub <= 0) return 0;
+  return BF16 ? int64_t(kMaxPrefillWorkgroups) : std::min<int64_t>(items_ub, 1024);
 }
 
 template <bool BF16, int D, int HW>

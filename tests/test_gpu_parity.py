@@ -56,7 +56,7 @@ def row_checksums(pool, dtype, chunk=16384):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6, 9])
 def test_config_parity(pa, cfg):
     wl = W.config_workload(cfg, hbm_bytes=hbm_bytes())
     say(f"[cfg {cfg}] {wl.name}: S={wl.num_seqs} T={wl.num_tokens} NB={wl.num_blocks}")

@@ -240,6 +240,7 @@ CONFIG_NAMES = {
     6: "llama3_8b_spec_verify_bf16",
     7: "llama3_70b_32k_decode_fp8kv",
     8: "llama3_8b_mixed_prefill_decode_fp8kv",
+    9: "llama3_8b_long_prompt_last_chunk_bf16",
 }
 
 DEFAULT_HBM_BYTES = 288 * (1 << 30)
@@ -251,7 +252,8 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
     1-5 are the path's configurations; 6 is speculative-decode verification
     (short multi-token queries over long contexts); 7 and 8 are the 70B 32k
     decode and the 8B mixed step over an 8-bit (fp8) KV pool (the 70B pool
-    again ~60% of HBM, in 32 KiB blocks)."""
+    again ~60% of HBM, in 32 KiB blocks); 9 is the last 512-token chunk of a
+    32,512-token prompt with Llama-3-8B heads (a few long prefill items)."""
     name = CONFIG_NAMES[cfg]
     if cfg == 7:
         hbm = DEFAULT_HBM_BYTES if hbm_bytes is None else int(hbm_bytes)
@@ -288,6 +290,8 @@ def config_workload(cfg: int, *, hbm_bytes: Optional[int] = None) -> Workload:
         C = r.integers(1024, 8192, size=256, endpoint=True)
         return build_workload(name, "bf16", 32, 8, 128, C, np.full(256, 4, np.int64), seed=cfg,
                               max_blocks=(8192 + 4) // BLOCK_SIZE + 1)
+    if cfg == 9:
+        return build_workload(name, "bf16", 32, 8, 128, np.array([32000]), np.array([512]), seed=cfg)
     raise ValueError(f"unknown config {cfg}")
 
 
