@@ -152,10 +152,14 @@ def beside_cases():
     # with tokens enough for the library to take the two-stream path
     cases.append(W.build_workload("beside_decode_only", "bf16", 32, 8, 128, [5, 2500, 900, 0], [1, 4, 4, 4],
                                   seed=911, max_blocks=16384))
+    # one chunk after a long context next to decodes: its 8 items outlast an
+    # equal share of the few CUs the prefill gets, so the schedule cuts them
+    cases.append(W.build_workload("beside_long_chunk", "bf16", 32, 8, 128, [30000, 700, 5000, 12, 9000],
+                                  [64, 1, 1, 1, 1], seed=912, max_blocks=16384))
     return cases
 
 
-@pytest.mark.parametrize("idx", range(6))
+@pytest.mark.parametrize("idx", range(7))
 def test_prefill_beside_decode(pa, idx):
     wl = beside_cases()[idx]
     bound = wl.num_seqs * wl.max_blocks * 16 * 2 * wl.num_kv_heads * wl.head_size * 2
