@@ -1187,11 +1187,11 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
     if (tid == 0) st[1] = cuts ? st[1] + 1 : nwg + claimed;
     // A cut item: this piece's partial result goes to the workspace, and the
     // piece that counts in last combines every piece's.
-    const int npieces_e = CUTS ? __builtin_amdgcn_readfirstlane(st_rd[5]) : 1;
-    bool merge = false;
-    if (npieces_e > 1) {
-      const int npieces = npieces_e, pidx = __builtin_amdgcn_readfirstlane(st_rd[6]);
-      const int64_t merge_slot = __builtin_amdgcn_readfirstlane(st_rd[7]);
+    // (the piece's index and count and its item's counter, from LDS)
+    const int cut_n = CUTS ? __builtin_amdgcn_readfirstlane(st_rd[5]) : 1;
+    if (cut_n > 1) {
+      const int cut_i = __builtin_amdgcn_readfirstlane(st_rd[6]);
+      const int64_t cut_slot = __builtin_amdgcn_readfirstlane(st_rd[7]);
       const int64_t row_bytes = a.Hq * a.max_parts * D * 4;  // workspace stride between tokens
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave is done with the stages
       // The wave's unnormalised 32 x D output, fp32, as rows in LDS (one
@@ -1240,20 +1240,20 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
           const u32x4 v = *reinterpret_cast<const lds_u32x4*>(rd + prow + 16u * (r * FCH + (c ^ (r % FCH))));
           if (i0 + r < n)
             __builtin_amdgcn_raw_buffer_store_b128(
-                v, ors, static_cast<uint32_t>(r * row_bytes + (pidx * D + 4 * c) * 4), 0, kCoherent);
+                v, ors, static_cast<uint32_t>(r * row_bytes + (cut_i * D + 4 * c) * 4), 0, kCoherent);
         }
         if (ln < 32 && i0 + ln < n) {
           const u32x2 v = *reinterpret_cast<const lds_u32x2*>(rd + pml + 8u * ln);
-          __builtin_amdgcn_raw_buffer_store_b64(v, mrs, static_cast<uint32_t>(ln) * ml_stride + 8u * pidx, 0, kCoherent);
+          __builtin_amdgcn_raw_buffer_store_b64(v, mrs, static_cast<uint32_t>(ln) * ml_stride + 8u * cut_i, 0, kCoherent);
         }
       }
       // Count this piece in once every wave's stores have completed.
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       if (tid == 0)
-        st[0] = __hip_atomic_fetch_add(a.sched + kMaxPrefillWorkgroups + merge_slot, 1, __ATOMIC_RELAXED,
+        st[0] = __hip_atomic_fetch_add(a.sched + kMaxPrefillWorkgroups + cut_slot, 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-      merge = __builtin_amdgcn_readfirstlane(st_rd[0]) == npieces - 1;
+      const bool merge = __builtin_amdgcn_readfirstlane(st_rd[0]) == cut_n - 1;
       if (merge && wave_active) {
         // Combine the pieces in piece order (online: rescale the running sum
         // to each new maximum), this one's rows from LDS, the others' from the
@@ -1278,9 +1278,9 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
             m_off[i] = static_cast<uint32_t>(rr) * ml_stride;
           }
 #pragma unroll 1
-          for (int p = 0; p < npieces; ++p) {
+          for (int p = 0; p < cut_n; ++p) {
             float mp[NP], lp[NP], op[NP][4];
-            if (p == pidx) {
+            if (p == cut_i) {
 #pragma unroll
               for (int i = 0; i < NP; ++i) {
                 const int r = (half * NP + i) * RPR + ln / FCH;
@@ -1332,7 +1332,7 @@ __device__ __attribute__((always_inline)) inline void prefill_bf16_items(const A
         }
       }
     }
-    if (npieces_e == 1 && wave_active) {
+    if (cut_n == 1 && wave_active) {
       // The wave's 32 x D output tile goes out as whole rows: the lanes hold
       // it transposed (lane (col, hh) has O^T[d = 32 dt + 8 q + 4 hh + r][token
       // col], 8-byte pieces of 32 different rows per store), so it passes
