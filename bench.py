@@ -249,7 +249,7 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         "kernels": kern,
         "output_finite": finite,
     }
-    if "decode" in kern:
+    if "decode" in kern and dec_kernel_bytes > 0:  # (a batch with no decode-kernel sequence has no decode rate)
         d = kern["decode"]["avg_ms"]
         r["decode_kernel_bytes"] = dec_kernel_bytes
         r["decode_kernel_gbs"] = dec_kernel_bytes / (d * 1e-3) / 1e9
