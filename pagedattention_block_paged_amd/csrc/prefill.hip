@@ -146,7 +146,8 @@ __device__ void plan_body(const int32_t* qsl, const int32_t* ctx_lens,
   __shared__ int32_t n_active;
   __shared__ float red_dec[1024], red_pre[1024];
   __shared__ uint64_t keys[kMaxSortedTiles];
-  __shared__ int32_t tile_seq[kMaxSortedTiles];  // sequence of each tile (sorted case)
+  // sequence of each tile (sorted case); later reused as int64 scratch, hence 8-byte aligned
+  __shared__ __attribute__((aligned(8))) int32_t tile_seq[kMaxSortedTiles];
   const int tid = threadIdx.x;
   const int64_t per = (S + 1023) / 1024;
   const int64_t s0 = min(S, tid * per), s1 = min(S, s0 + per);
