@@ -229,7 +229,7 @@ pa_status pa_step_noalloc(const pa_tensor* out, const pa_tensor* q, const pa_ten
  * Bytes of workspace pa_attention / pa_step need for these extents (the
  * split-K partial results, one set per new token of the sequences the decode
  * kernel attends -- those whose query length times Hq / Hkv is at most 16 --
- * and the prefill tile list).
+ * the prefill tile list, and the decode's work order).
  * Returns 0 for invalid extents.
  */
 size_t pa_attention_workspace_size(int64_t num_seqs, int64_t num_tokens, int64_t num_q_heads,

@@ -9,7 +9,9 @@
  * Kernel ids: 0 KV write, 1 decode (split-K partitions), 2 partition reduce,
  * 3 prefill plan, 4 chunked prefill (which also combines the decode's
  * partitions when it runs after the decode on the launch stream), 5 KV write
- * and plan in one launch (steps whose prefill runs after the decode).
+ * and plan in one launch (steps whose prefill runs after the decode), 6 the
+ * decode's work order (ahead of decode launches of more than one round of
+ * workgroups).
  */
 #ifndef PA_PROFILE_H_
 #define PA_PROFILE_H_
@@ -20,7 +22,7 @@
 extern "C" {
 #endif
 
-#define PA_PROFILE_KERNELS 6
+#define PA_PROFILE_KERNELS 7
 
 /* Drop earlier records and start recording. Returns 0 (PA_OK). */
 int pa_profile_start(void);

@@ -41,7 +41,7 @@ EXPORTS = ("pa_reshape_and_cache", "pa_attention", "pa_step", "pa_reshape_and_ca
            "pa_last_error", "pa_version")
 PROFILE_EXPORTS = ("pa_profile_start", "pa_profile_stop", "pa_profile_kernel", "pa_profile_kernel_name",
                    "pa_profile_read_probe")
-KERNELS = ("kv_write", "decode", "partition_reduce", "prefill_plan", "prefill", "kv_write_plan")
+KERNELS = ("kv_write", "decode", "partition_reduce", "prefill_plan", "prefill", "kv_write_plan", "decode_order")
 
 
 class PAError(RuntimeError):

@@ -398,24 +398,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wph = kDecodeWaves / hw;  // waves per KV head
   const uint32_t n_hg = static_cast<uint32_t>(a.Hkv / hw);
-  const uint32_t s = blockIdx.x / n_hg, hg = blockIdx.x - s * n_hg;
+  // The workgroup's unit x = s * n_hg + hg and partition p, with the
+  // sequence's query rows [q0, q1), length and cached context: the next
+  // record of the work order (longest first) when the launch has one, else
+  // the grid position.
+  uint32_t x;
+  int p, q0, q1, len_s, ctx_s;
+  if (a.dorder != nullptr) {
+    const uint32_t b = blockIdx.x;  // an ordered launch has a 1-D grid
+    const int4* rec = reinterpret_cast<const int4*>(a.dorder + kDecodeOrderHeader) + 2 * b;
+    const int n_work = a.dorder[0];
+    const int4 r0 = rec[0], r1 = rec[1];
+    // every value taken here, so that the compiler issues the loads together
+    // (one round trip) instead of waiting for the count before the record
+    asm volatile("" ::"s"(n_work), "s"(r0.x), "s"(r0.y), "s"(r0.z), "s"(r0.w), "s"(r1.x), "s"(r1.y));
+    if (static_cast<int64_t>(b) >= n_work) return;  // whole workgroup
+    x = static_cast<uint32_t>(r0.x);
+    p = r0.y;
+    q0 = r0.z;
+    q1 = r0.w;
+    len_s = r1.x;
+    ctx_s = r1.y;
+  } else {
+    x = blockIdx.x;
+    p = blockIdx.y;
+    const uint32_t s0 = x / n_hg;
+    q0 = a.qsl[s0];
+    q1 = a.qsl[s0 + 1];
+    len_s = a.seq_lens[s0];
+    ctx_s = a.ctx_lens[s0];
+  }
+  const uint32_t s = x / n_hg, hg = x - s * n_hg;
   const uint32_t g = hg * hw + wave % hw;
   const int phase = wave / hw;
-  const int p = blockIdx.y;
-  const int q0 = a.qsl[s], q1 = a.qsl[s + 1];
   const int G = static_cast<int>(a.Hq / a.Hkv);
   const int nq = q1 - q0;  // new tokens of the sequence
   // this kernel's sequences only (whole workgroup); the rows must lie in [0, T)
   if (!decode_path(nq, G) || q0 < 0 || q1 > a.T) return;
   const int PT = static_cast<int>(a.part_tokens);
-  const int L = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), a.MB * kBlockTokens));
+  const int L = static_cast<int>(min(max(static_cast<int64_t>(len_s), int64_t(0)), a.MB * kBlockTokens));
   const int start = p * PT;
   if (start >= L) return;  // whole workgroup
   const int end = min(start + PT, L);
   const int nparts = (L + PT - 1) / PT;
   const int ncol = nq * G;  // columns (token i, head h) = i * G + h
   // Column n is new token n / G at position C + n / G: it sees keys up to there.
-  const int C = min(max(a.ctx_lens[s], 0), L);
+  const int C = min(max(ctx_s, 0), L);
   const int lim = min(end, C + n / G + 1);
   const float qk_scale = a.scale * kLog2e * (KV8 ? a.k_scale : 1.f);
   const int b0 = start / kBlockTokens;
@@ -548,6 +576,87 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   combine_waves<BF16, D, KV8>(a, smem, wstride, hw, wph, ncol, hg, G, q0, nparts, p);
 }
 
+// The decode's work order. Workgroups start in grid order as CUs free up, so
+// a launch of several rounds that happens to dispatch long partitions last
+// ends with a few CUs streaming them alone, each at the rate of its waves'
+// few loads in flight, while the rest of the GPU idles. One workgroup sorts
+// the launch's (sequence, head group, partition) units by the partition's
+// token count, longest first (a counting sort over kOrderBuckets length
+// classes; the order within a class is whatever the LDS atomics give, which
+// no result depends on), and writes one record per unit for the decode
+// kernel: [0] of dorder gets the count. Units are exactly those the decode
+// kernel would attend from its grid position.
+constexpr int kOrderBuckets = 256;
+constexpr int kOrderThreads = 1024;
+
+__global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(AttnArgs a, int hw) {
+  __shared__ int32_t count[kOrderBuckets];
+  __shared__ int32_t next[kOrderBuckets];
+  const int tid = threadIdx.x;
+  const int n_hg = static_cast<int>(a.Hkv / hw);
+  const int64_t G = a.Hq / a.Hkv;
+  const int PT = static_cast<int>(a.part_tokens);
+  const int64_t max_len = a.MB * kBlockTokens;
+  for (int i = tid; i < kOrderBuckets; i += kOrderThreads) count[i] = 0;
+  __syncthreads();
+  // Partitions of sequence s that the decode kernel attends (0 if none).
+  auto parts_of = [&](int64_t s, int& q0, int& q1, int& len) {
+    q0 = a.qsl[s];
+    q1 = a.qsl[s + 1];
+    if (!decode_path(q1 - q0, G) || q0 < 0 || q1 > a.T) return 0;
+    len = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), max_len));
+    return (len + PT - 1) / PT;
+  };
+  // class of a partition of `tok` tokens (1 .. PT): 0 for the longest
+  auto bucket = [&](int tok) { return kOrderBuckets - 1 - (tok - 1) * kOrderBuckets / PT; };
+  for (int64_t s = tid; s < a.S; s += kOrderThreads) {
+    int q0, q1, len;
+    const int np = parts_of(s, q0, q1, len);
+    for (int p = 0; p < np; ++p) atomicAdd(&count[bucket(min(PT, len - p * PT))], n_hg);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < kOrderBuckets; ++i) {
+      next[i] = run;
+      run += count[i];
+    }
+    a.dorder[0] = run;
+  }
+  __syncthreads();
+  int4* const rec = reinterpret_cast<int4*>(a.dorder + kDecodeOrderHeader);
+  for (int64_t s = tid; s < a.S; s += kOrderThreads) {
+    int q0, q1, len;
+    const int np = parts_of(s, q0, q1, len);
+    if (np == 0) continue;
+    const int ctx = a.ctx_lens[s], len_raw = a.seq_lens[s];
+    for (int p = 0; p < np; ++p) {
+      const int at = atomicAdd(&next[bucket(min(PT, len - p * PT))], n_hg);
+      for (int hg = 0; hg < n_hg; ++hg) {
+        rec[2 * (at + hg)] = make_int4(static_cast<int>(s) * n_hg + hg, p, q0, q1);
+        rec[2 * (at + hg) + 1] = make_int4(len_raw, ctx, 0, 0);
+      }
+    }
+  }
+}
+
+// Whether a decode launch takes the work order: more units than one round of
+// workgroups, units that can be long enough for a late one to matter (the
+// order costs a launch and about 25 us for 4,000 sequences; a 1024-token
+// unit streamed alone at the end takes longer), no more units than the
+// workspace holds records for, and not switched off with PA_DECODE_ORDER=0
+// in the environment (read at each launch).
+constexpr int64_t kOrderMinTokens = 1024;
+
+bool decode_ordered(const AttnArgs& a, int hw, int per_cu) {
+  if (a.dorder == nullptr) return false;
+  const int64_t units = a.S * (a.Hkv / hw) * a.max_parts;
+  if (units <= int64_t(256) * (per_cu > 0 ? per_cu : 1) || units > kMaxOrderedUnits) return false;
+  if (std::min(a.part_tokens, a.MB * kBlockTokens) < kOrderMinTokens) return false;
+  const char* e = std::getenv("PA_DECODE_ORDER");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
+
 // Combine the partitions of multi-partition sequences of the decode kernel
 // (step_parts.h): one wave per (sequence, query head), in fixed partition
 // order.
@@ -614,9 +723,22 @@ hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce
   const dim3 grid(static_cast<unsigned>(a.S * (a.Hkv / hw)), static_cast<unsigned>(a.max_parts));
   const hipError_t attr = allow_decode_lds<BF16, D, KV8>();
   if (attr != hipSuccess) return attr;
+  // An ordered launch takes its units from the work order, one per
+  // workgroup of a 1-D grid of the same size.
+  AttnArgs b = a;
+  dim3 g = grid;
+  if (decode_ordered(a, hw, decode_occupancy<BF16, D, KV8>())) {
+    ProfileScope ps(kDecodeOrder, stream);
+    hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, b, hw);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g = dim3(grid.x * grid.y);
+  } else {
+    b.dorder = nullptr;
+  }
   {
     ProfileScope ps(kDecode, stream);
-    hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV8>), grid, dim3(kDecodeThreads), lds, stream, a, a.block_tables,
+    hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV8>), g, dim3(kDecodeThreads), lds, stream, b, b.block_tables,
                        hw);
   }
   hipError_t e = hipGetLastError();

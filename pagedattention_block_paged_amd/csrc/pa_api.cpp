@@ -321,6 +321,7 @@ pa_status validate_attention(const pa_tensor* out, const pa_tensor* q, const pa_
   a->work_counter = reinterpret_cast<int32_t*>(base + wl.counter_off);
   a->tile_order = reinterpret_cast<int32_t*>(base + wl.order_off);
   a->sched = reinterpret_cast<int32_t*>(base + wl.sched_off);
+  a->dorder = reinterpret_cast<int32_t*>(base + wl.dorder_off);
   a->ws_ml = reinterpret_cast<float2*>(base + wl.ml_off);
   a->ws_o = reinterpret_cast<float*>(base + wl.o_off);
   return PA_OK;
@@ -377,8 +378,11 @@ constexpr double kBesideMinDecodeBytes = 4e9;
 // (a sequence on the prefill path has more than 16 / G new tokens), so that
 // batches of decodes alone do not pay for an idle second stream.
 bool prefill_beside_decode(const pa::AttnArgs& a) {
-  if (a.elem != pa::Elem::BF16) return false;
-  const double kv_bytes = a.kv8 ? 1.0 : 2.0;
+  // bf16 pools only: the prefill of an 8-bit pool widens each tile through
+  // registers, and beside the decode's HBM stream it ran 2.5-3x slower than
+  // alone, past the decode's end; after the decode it takes about 0.3 ms.
+  if (a.elem != pa::Elem::BF16 || a.kv8) return false;
+  const double kv_bytes = 2.0;
   const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * kv_bytes;
   const int64_t G = a.Hq / a.Hkv;
   return kv_bound >= kBesideMinDecodeBytes && a.T - a.S >= pa::kMaxDecodeColumns / G + 1;
@@ -456,7 +460,10 @@ WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, 
   w.counter_off = align(size_t(S + 1) * sizeof(int32_t));
   w.order_off = w.counter_off + 256;
   w.sched_off = w.order_off + align(size_t(kMaxSortedTiles) * kTileRecord * sizeof(int32_t));
-  w.ml_off = w.sched_off + align(size_t(2 * kMaxPrefillWorkgroups) * sizeof(int32_t));
+  w.dorder_off = w.sched_off + align(size_t(2 * kMaxPrefillWorkgroups) * sizeof(int32_t));
+  // the decode's work order: one record per (sequence, head group, partition)
+  const int64_t units = std::min(S * (Hkv / decode_heads_per_workgroup(Hkv)) * parts, kMaxOrderedUnits);
+  w.ml_off = w.dorder_off + align(size_t(kDecodeOrderHeader + units * kDecodeOrderRecord) * sizeof(int32_t));
   // split-K partials, one set per (new token, query head, partition): the
   // decode kernel's sequences use them for their partitions, and the bf16
   // prefill for the key-range pieces of its split items (the rows of the

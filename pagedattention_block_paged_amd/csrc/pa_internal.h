@@ -92,6 +92,9 @@ struct AttnArgs {
                           // cost capacity per workgroup (int64, low word first)
   int32_t* sched;         // [kMaxPrefillWorkgroups] first item of each bf16 prefill workgroup, then
                           // [kMaxPrefillWorkgroups] merge counters of split items (both set by the plan kernel)
+  int32_t* dorder;        // the decode workgroups' work, longest first: [0] count, then from word
+                          // kDecodeOrderHeader one kDecodeOrderRecord-word record per workgroup (set by
+                          // decode_order_kernel; read by the decode kernel when its launch is ordered)
 };
 
 // The bf16 prefill launches at most one workgroup per CU.
@@ -102,8 +105,17 @@ constexpr int kMaxPrefillWorkgroups = 256;
 constexpr int kMaxSortedTiles = 4096;
 constexpr int kTileRecord = 16;  // int32 words per ranked-tile record
 
+// Decode work order: a launch whose grid holds more than one round of
+// workgroups takes its (sequence, head group, partition) units longest
+// first. A record: unit x = sequence * head groups + group, partition, the
+// sequence's query start and end, its length and cached context (as in the
+// caller's arrays), 2 unused. At most kMaxOrderedUnits units are ordered.
+constexpr int kDecodeOrderHeader = 64;  // int32 words before the first record
+constexpr int kDecodeOrderRecord = 8;   // int32 words per record
+constexpr int64_t kMaxOrderedUnits = int64_t(1) << 20;
+
 struct WorkspaceLayout {
-  size_t tile_start_off, counter_off, order_off, sched_off, ml_off, o_off, total;
+  size_t tile_start_off, counter_off, order_off, sched_off, dorder_off, ml_off, o_off, total;
 };
 
 // Tokens per split-K decode partition. per_cu: decode workgroups a CU holds at
@@ -112,7 +124,7 @@ int64_t partition_tokens(int64_t S, int64_t Hkv, int64_t MB, int per_cu);
 WorkspaceLayout workspace_layout(int64_t S, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int64_t MB);
 
 // Optional per-kernel HIP-event timing (include/pa_profile.h).
-enum KernelId { kKvWrite = 0, kDecode = 1, kReduce = 2, kPlan = 3, kPrefill = 4, kWritePlan = 5 };
+enum KernelId { kKvWrite = 0, kDecode = 1, kReduce = 2, kPlan = 3, kPrefill = 4, kWritePlan = 5, kDecodeOrder = 6 };
 bool profiling();
 void profile_mark(int id, bool end, hipStream_t stream);
 struct ProfileScope {

@@ -91,20 +91,16 @@ constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 
-// Cost model for running the prefill beside the decode kernel (measured on
-// MI355X at head size 128): a CU of the bf16 prefill kernel computes about
-// 4.7 TFLOP/s (the fp32-MFMA kernel that serves 8-bit pools about 0.36) and
-// spends about 6 us per item outside its key loop; the decode reads about
-// 6.6 TB/s over all 256 CUs.
+// Cost model for running the prefill beside the decode kernel, which only
+// bf16 steps over a bf16 pool do (measured on MI355X at head size 128): a CU
+// of the bf16 prefill kernel computes about 4.7 TFLOP/s and spends about
+// 6 us per item outside its key loop; the decode reads about 6.6 TB/s over
+// all 256 CUs. The prefill gets ratio * 256 * prefill work / (prefill +
+// decode work) CUs, ratio 2: the share would finish in about half the
+// decode's time alone, and beside the decode's HBM stream it takes most of
+// it; the HBM-bound decode barely notices the CUs it lost.
 constexpr float kPrefillFlopPerCuUs = 4.7e6f;
-constexpr float kPrefillF32FlopPerCuUs = 0.36e6f;
-constexpr int kThreadsPerCuF32 = 4 * kThreads;  // the fp32 kernel runs 4 workgroups per CU
-// CUs given to the prefill beside the decode: ratio * 256 * prefill work /
-// (prefill + decode work). 2 for the bf16 kernel (its share then finishes in
-// about half the decode's time, and the HBM-bound decode barely notices the
-// CUs it lost); the decode of an 8-bit pool reads half the bytes and notices
-// more, so the slower fp32 kernel gets a smaller share.
-constexpr float kBesideRatioF32 = 1.0f;
+constexpr float kBesideRatio = 2.0f;
 constexpr float kPrefillItemCuUs = 6.0f;
 constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
 
@@ -1620,9 +1616,10 @@ PlanArgs plan_args(const AttnArgs& a, int64_t slots, bool beside) {
   p.items_per_tile = static_cast<int>(a.Hkv * (a.Hq / a.Hkv / HW));
   p.slots = static_cast<int>(slots);
   p.beside = beside ? 1 : 0;
-  p.flop_per_cu_us = BF16 ? kPrefillFlopPerCuUs : kPrefillF32FlopPerCuUs;
-  p.wg_per_cu = BF16 ? 1 : kThreadsPerCuF32 / kThreads;
-  p.ratio = BF16 ? 2.f : kBesideRatioF32;
+  // (the share beside the decode: bf16 kernel only)
+  p.flop_per_cu_us = kPrefillFlopPerCuUs;
+  p.wg_per_cu = 1;
+  p.ratio = kBesideRatio;
   p.tile_start = a.tile_start;
   p.tile_order = a.tile_order;
   p.counter = a.work_counter;

@@ -22,7 +22,7 @@ std::vector<hipEvent_t> g_free;
 thread_local hipEvent_t t_open[PA_PROFILE_KERNELS] = {};
 
 const char* const kNames[PA_PROFILE_KERNELS] = {"kv_write", "decode", "partition_reduce", "prefill_plan",
-                                                "prefill", "kv_write_plan"};
+                                                "prefill", "kv_write_plan", "decode_order"};
 
 hipEvent_t take_event() {
   {

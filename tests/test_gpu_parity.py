@@ -263,6 +263,59 @@ def test_repeated_calls_are_deterministic(pa):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+ORDER_CASES = [  # (dtype, Hq, Hkv, D, decodes, longest context, seed): more units than one round of workgroups
+    ("bf16", 8, 2, 128, 400, 8000, 81),   # one head group per sequence, up to 2 partitions of 4096
+    ("bf16", 16, 16, 64, 150, 10000, 82),  # two head groups (16 KV heads), up to 3 partitions of 4096
+    ("f32", 8, 2, 64, 600, 8000, 83),
+]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("idx", range(len(ORDER_CASES)))
+def test_decode_work_order(pa, idx, monkeypatch):
+    """A decode launch of more than one round of workgroups takes its
+    (sequence, head group, partition) units longest first, from a work order
+    that a one-workgroup kernel writes ahead of it. Every unit is computed as
+    in grid order, so the output equals the grid-order launch's
+    (PA_DECODE_ORDER=0) bit for bit; and the oracle's on every row. The batch
+    mixes decodes of one to three partitions, short multi-token queries (also
+    on the decode kernel) and a prefill chunk (not in the order)."""
+    dtype, Hq, Hkv, D, S, Lmax, seed = ORDER_CASES[idx]
+    rs = np.random.default_rng(seed)
+    G = Hq // Hkv
+    ctx = list(rs.integers(0, Lmax, size=S))
+    ql = [1] * S
+    nmax = 16 // G
+    for i in range(0, S, 37):  # short multi-token queries
+        ql[i] = int(rs.integers(1, nmax + 1))
+    ctx.append(300)
+    ql.append(nmax + 40)  # a chunk for the prefill kernel
+    mb = -(-(Lmax + 64) // 16)
+    wl = W.build_workload(f"order{idx}", dtype, Hq, Hkv, D, ctx, ql, seed=seed, max_blocks=mb)
+    pt = pa.partition_tokens(wl.num_seqs, Hkv, D, dtype, wl.max_blocks)
+    hw = next(h for h in (8, 4, 2, 1) if Hkv % h == 0)
+    units = wl.num_seqs * (Hkv // hw) * (-(-wl.max_blocks * 16 // pt))
+    say(f"[order {idx}] {dtype} Hq={Hq} Hkv={Hkv} D={D} S={wl.num_seqs} partition={pt} units={units}")
+    assert units > 512, "the case must take the ordered launch"
+    c = device_case(wl)
+    ws = pa.new_workspace(c["q"], c["pool"][:, 0], c["block_tables"])
+    with pa.profile() as prof:
+        ordered = run_step(pa, wl, c, workspace=ws).clone()
+        torch.cuda.synchronize()
+    assert "decode_order" in prof.kernels, prof.kernels
+    monkeypatch.setenv("PA_DECODE_ORDER", "0")
+    with pa.profile() as prof:
+        grid = run_step(pa, wl, c, workspace=ws).clone()
+        torch.cuda.synchronize()
+    assert "decode_order" not in prof.kernels, prof.kernels
+    iv = torch.int16 if dtype == "bf16" else torch.int32
+    assert torch.equal(ordered.view(iv), grid.view(iv))
+    e = oracle_every_row(wl, ordered, lambda sub, hp: oracle.run_workload(sub, pool=hp), say=say).summary()
+    say(f"[order {idx}] {e}")
+    assert e["rows"] == wl.num_tokens * wl.num_q_heads
+    assert_summary(e, dtype, wl.name)
+
+
 def test_partition_size_counts_resident_workgroups(pa):
     """The partition size gives one round of decode workgroups: the bf16
     kernel at head size 128 fits one workgroup per CU, the 8-bit-pool kernel
