@@ -17,8 +17,9 @@ runs every part of the path. `value` is its decode KV-read bandwidth over the
 whole step; the line also carries mixed-step tokens/s, prefill TFLOP/s and the
 roofline of the decode (HBM) and prefill (bf16 MFMA, nested as
 roofline.prefill) kernels. In this step the library runs the prefill kernel
-beside the decode kernel on a few CUs, so the prefill roofline is timed on the
-same chunks run alone. `secondary` holds the other workloads -- the tiny fp32
+after the decode kernel, first combining the decode's split-K partitions (the
+chunks are too small a share of the step to gain from running beside the
+decode), so the prefill roofline is timed on the same chunks run alone. `secondary` holds the other workloads -- the tiny fp32
 decode, the TinyLlama-1.1B decode batch, the Llama-3-70B 32k decode, the
 shared-prefix decode, a speculative-decode verification batch (4 new tokens
 per sequence over long contexts), the 70B decode and 8B mixed step over an
@@ -278,6 +279,8 @@ def measure(cfg: int, steps: int, warmup: int, flush: str = "read", graph: bool 
         if alone:
             r["prefill_alone"] = alone
             r["prefill_in_step_ms"] = kern["prefill"]["avg_ms"]
+            # the two-stream path launches the plan on its own ("prefill_plan")
+            r["prefill_beside_decode"] = "prefill_plan" in kern
     r["flush"] = flush
     del c, pool, out, ws, scratch
     torch.cuda.empty_cache()
@@ -529,7 +532,8 @@ def kernel_traffic(kernel: str, workload: str):
 def prefill_timing_note(head: dict) -> str:
     if not head.get("prefill_alone"):
         return "in the step"
-    where = "beside the decode on a few CUs, hidden behind it"
+    where = ("beside the decode on a few CUs, hidden behind it" if head.get("prefill_beside_decode")
+             else "after the decode on the whole GPU, first combining the decode's partitions")
     return f"the step's prefill chunks alone; in the step the kernel runs {where} ({head['prefill_in_step_ms']:.3f} ms)"
 
 

@@ -372,25 +372,39 @@ SideStream* side_stream_for(hipStream_t stream) {
 // width. Above this the decode kernel runs long enough that running the
 // prefill beside it pays for the cross-stream hand-off (a few microseconds).
 constexpr double kBesideMinDecodeBytes = 4e9;
+// The prefill's share of the work, both at the table's full width: every
+// query token past one per sequence against every key at the bf16 prefill
+// kernel's rate, against every sequence's keys at the decode's HBM rate.
+// Below this, running the prefill after the decode on the whole GPU costs
+// less than sharing the GPU: on the Llama-3-8B decode batch (4,096 sequences
+// of up to 8,192 tokens) with 8 chunks of 512 tokens (2% here) the step took
+// 10.64 ms after against 10.74 ms beside; with 64 chunks (17%) 11.76 against
+// 11.06 ms, with 160 (42%) 13.57 against 12.42 ms.
+constexpr double kBesideMinPrefillShare = 0.05;
 
-// Whether the prefill runs beside the decode: bf16, a decode that may be long,
-// and more query tokens than one per sequence by at least one prefill chunk
-// (a sequence on the prefill path has more than 16 / G new tokens), so that
-// batches of decodes alone do not pay for an idle second stream.
+// Whether the prefill runs beside the decode: bf16 queries over a bf16 pool,
+// a decode that may be long, at least one sequence's worth of tokens past
+// one per sequence (a sequence on the prefill path has more than 16 / G new
+// tokens; batches of single-token decodes never qualify), and a prefill
+// share of at least kBesideMinPrefillShare.
 bool prefill_beside_decode(const pa::AttnArgs& a) {
   // bf16 pools only: the prefill of an 8-bit pool widens each tile through
   // registers, and beside the decode's HBM stream it ran 2.5-3x slower than
   // alone, past the decode's end; after the decode it takes about 0.3 ms.
-  if (a.elem != pa::Elem::BF16 || a.kv8) return false;
-  const double kv_bytes = 2.0;
-  const double kv_bound = double(a.S) * double(a.MB) * pa::kBlockTokens * 2.0 * double(a.Hkv) * double(a.D) * kv_bytes;
+  if (a.elem != pa::Elem::BF16 || a.kv8 || a.S <= 0) return false;
   const int64_t G = a.Hq / a.Hkv;
-  return kv_bound >= kBesideMinDecodeBytes && a.T - a.S >= pa::kMaxDecodeColumns / G + 1;
+  if (a.T - a.S < pa::kMaxDecodeColumns / G + 1) return false;
+  const double keys = double(a.MB) * pa::kBlockTokens;
+  const double decode_bytes = double(a.S) * keys * 2.0 * double(a.Hkv) * double(a.D) * 2.0;
+  const double decode_work = decode_bytes / pa::kDecodeBytePerCuUs;
+  const double prefill_work = double(a.T - a.S) * keys * 4.0 * double(a.Hq) * double(a.D) / pa::kPrefillFlopPerCuUs;
+  return decode_bytes >= kBesideMinDecodeBytes && prefill_work >= kBesideMinPrefillShare * decode_work;
 }
 
 // The decode kernel (HBM-bound) and the chunked prefill (MFMA-bound) work on
-// disjoint rows of `out` and read only the inputs. For large mixed batches in
-// bf16 the prefill runs on a second stream, forked from and joined back into
+// disjoint rows of `out` and read only the inputs. For large bf16 batches
+// with a large enough prefill (prefill_beside_decode) the prefill runs on a
+// second stream, forked from and joined back into
 // `stream`, on a few CUs chosen by the plan kernel while the decode streams
 // on the rest. Otherwise everything runs on `stream`: the plan (unless the
 // caller's KV write launch already made it), the decode, then the prefill

@@ -97,6 +97,12 @@ struct AttnArgs {
                           // decode_order_kernel; read by the decode kernel when its launch is ordered)
 };
 
+// Rates measured on MI355X at head size 128, for the choice and sizing of
+// the prefill beside the decode: a CU of the bf16 prefill kernel computes
+// about 4.7 TFLOP/s; the decode kernel reads about 6.6 TB/s over all 256 CUs.
+constexpr float kPrefillFlopPerCuUs = 4.7e6f;
+constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
+
 // The bf16 prefill launches at most one workgroup per CU.
 constexpr int kMaxPrefillWorkgroups = 256;
 

@@ -91,18 +91,16 @@ constexpr int kPWaves = 8;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int bf16_tile_tokens(int hw) { return kWaveTokens * (kPWaves / hw); }
 
-// Cost model for running the prefill beside the decode kernel, which only
-// bf16 steps over a bf16 pool do (measured on MI355X at head size 128): a CU
-// of the bf16 prefill kernel computes about 4.7 TFLOP/s and spends about
-// 6 us per item outside its key loop; the decode reads about 6.6 TB/s over
-// all 256 CUs. The prefill gets ratio * 256 * prefill work / (prefill +
-// decode work) CUs, ratio 2: the share would finish in about half the
-// decode's time alone, and beside the decode's HBM stream it takes most of
-// it; the HBM-bound decode barely notices the CUs it lost.
-constexpr float kPrefillFlopPerCuUs = 4.7e6f;
+// CUs of the prefill beside the decode kernel (bf16 steps over a bf16 pool
+// whose prefill is large enough, chosen on the host): ratio * 256 * prefill
+// work / (prefill + decode work), with the rates kPrefillFlopPerCuUs and
+// kDecodeBytePerCuUs, the prefill also paying about 6 us per item outside
+// its key loop. Ratio 2: the share would finish in about half the decode's
+// time alone; beside the decode's HBM stream it takes most of it, and the
+// HBM-bound decode barely notices the CUs it lost (ratio 4 ran 1.5-3.5%
+// slower on prefill-heavy steps).
 constexpr float kBesideRatio = 2.0f;
 constexpr float kPrefillItemCuUs = 6.0f;
-constexpr float kDecodeBytePerCuUs = 6.6e6f / 256.0f;
 
 // Static schedule of the bf16 prefill kernel. Costs are in quarters of a
 // 64-key tile: an item costs kItemFixedQ for its start and end plus 4 per
