@@ -180,6 +180,26 @@ def test_prefill_beside_decode(pa, idx):
     say(f"[beside {idx}] {e}")
 
 
+def test_small_prefill_share_runs_after_the_decode(pa):
+    """A block table as wide as the beside cases' but a prefill of under 5%
+    of the decode's bound work (one 40-token chunk next to 300 decodes): the
+    library runs the prefill after the decode on the caller's stream (the KV
+    write and the plan in one launch), and the result matches the oracle."""
+    rs = np.random.default_rng(4322)
+    ctx = [int(x) for x in rs.integers(0, 3000, size=300)] + [500]
+    ql = [1] * 300 + [40]
+    wl = W.build_workload("after_decode", "bf16", 32, 8, 128, ctx, ql, seed=913, max_blocks=16384)
+    bound = wl.num_seqs * wl.max_blocks * 16 * 2 * wl.num_kv_heads * wl.head_size * 2
+    assert bound >= 4e9
+    c = device_case(wl)
+    with pa.profile() as prof:
+        out = run_step(pa, wl, c)
+        torch.cuda.synchronize()
+    assert "kv_write_plan" in prof.kernels and "prefill_plan" not in prof.kernels, prof.kernels
+    ref, _ = oracle.run_workload(wl)
+    say(f"[after decode] {assert_within(to_f64(out), ref, wl.dtype, 'after decode')}")
+
+
 def test_chunked_prefill_matches_whole_prefill(pa):
     """18 tokens as chunks of 8 + 8 + 2 through one pool equal one 18-token prefill."""
     whole = W.build_workload("whole", "bf16", 8, 2, 128, [0], [18], seed=77, num_blocks=8)
