@@ -386,7 +386,7 @@ __device__ inline void combine_waves(const AttnArgs& a, const float* smem, int w
 // sweep, then each wave's (max, sum, output) for the merge.
 template <bool BF16, int D, int NPF, bool KV8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, const int32_t* __restrict__ bt_all,
-                                                                int hw) {
+                                                                int hw, int first_round) {
   static_assert(!KV8 || BF16, "8-bit pools compute in bf16");
   using Sh = DecodeShape<BF16, D>;
   constexpr int ES = Sh::ES, KC = Sh::KC, VE = Sh::VE;
@@ -399,13 +399,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
   const int wph = kDecodeWaves / hw;  // waves per KV head
   const uint32_t n_hg = static_cast<uint32_t>(a.Hkv / hw);
   // The workgroup's unit x = s * n_hg + hg and partition p, with the
-  // sequence's query rows [q0, q1), length and cached context: the next
-  // record of the work order (longest first) when the launch has one, else
-  // the grid position.
+  // sequence's query rows [q0, q1), length and cached context: a record of
+  // the work order (longest first) when the launch has one, else the grid
+  // position. Of an ordered launch (a 1-D grid), the first round of
+  // workgroups, which start together, take records 0 .. first_round - 1;
+  // each later one claims the next record as it starts. Workgroup b runs on
+  // XCD b mod 8, and the XCDs stream at different rates (in the 70B batch,
+  // one round of equal units, their mean finish times spread over 8%): with
+  // a fixed assignment every XCD gets an equal share of the order and the
+  // slowest ends last; with claims, the CUs of a slower XCD free up later
+  // and draw the shorter units at the end of the order.
   uint32_t x;
   int p, q0, q1, len_s, ctx_s;
   if (a.dorder != nullptr) {
-    const uint32_t b = blockIdx.x;  // an ordered launch has a 1-D grid
+    uint32_t b = blockIdx.x;
+    if (static_cast<int>(b) >= first_round) {
+      __shared__ int claimed;
+      if (threadIdx.x == 0) claimed = atomicAdd(a.dorder + 1, 1);
+      __syncthreads();
+      b = static_cast<uint32_t>(first_round + __builtin_amdgcn_readfirstlane(claimed));
+    }
     const int4* rec = reinterpret_cast<const int4*>(a.dorder + kDecodeOrderHeader) + 2 * b;
     const int n_work = a.dorder[0];
     const int4 r0 = rec[0], r1 = rec[1];
@@ -622,6 +635,7 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(AttnArgs a,
       run += count[i];
     }
     a.dorder[0] = run;
+    a.dorder[1] = 0;  // the decode's claim counter
   }
   __syncthreads();
   int4* const rec = reinterpret_cast<int4*>(a.dorder + kDecodeOrderHeader);
@@ -727,7 +741,10 @@ hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce
   // workgroup of a 1-D grid of the same size.
   AttnArgs b = a;
   dim3 g = grid;
-  if (decode_ordered(a, hw, decode_occupancy<BF16, D, KV8>())) {
+  const int per_cu = decode_occupancy<BF16, D, KV8>();
+  // workgroups that start together: 256 CUs times the kernel's occupancy
+  const int first_round = 256 * (per_cu > 0 ? per_cu : 1);
+  if (decode_ordered(a, hw, per_cu)) {
     ProfileScope ps(kDecodeOrder, stream);
     hipLaunchKernelGGL(decode_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, b, hw);
     const hipError_t e = hipGetLastError();
@@ -739,7 +756,7 @@ hipError_t launch_staged(const AttnArgs& a, hipStream_t stream, bool with_reduce
   {
     ProfileScope ps(kDecode, stream);
     hipLaunchKernelGGL((decode_kernel<BF16, D, 1, KV8>), g, dim3(kDecodeThreads), lds, stream, b, b.block_tables,
-                       hw);
+                       hw, first_round);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !with_reduce) return e;

@@ -92,9 +92,10 @@ struct AttnArgs {
                           // cost capacity per workgroup (int64, low word first)
   int32_t* sched;         // [kMaxPrefillWorkgroups] first item of each bf16 prefill workgroup, then
                           // [kMaxPrefillWorkgroups] merge counters of split items (both set by the plan kernel)
-  int32_t* dorder;        // the decode workgroups' work, longest first: [0] count, then from word
-                          // kDecodeOrderHeader one kDecodeOrderRecord-word record per workgroup (set by
-                          // decode_order_kernel; read by the decode kernel when its launch is ordered)
+  int32_t* dorder;        // the decode workgroups' work, longest first: [0] count, [1] the decode's claim
+                          // counter (zeroed), then from word kDecodeOrderHeader one kDecodeOrderRecord-word
+                          // record per unit (set by decode_order_kernel; read by the decode kernel when
+                          // its launch is ordered)
 };
 
 // Rates measured on MI355X at head size 128, for the choice and sizing of
