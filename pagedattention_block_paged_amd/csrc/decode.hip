@@ -378,7 +378,8 @@ __device__ inline void combine_waves(const AttnArgs& a, const float* smem, int w
 }
 
 // Workgroup: 8 waves, (sequence s, group of HW KV heads, partition p); grid
-// x = s * (Hkv / HW) + head group, y = p. Wave w serves KV head w % HW and,
+// x = s * (Hkv / HW) + head group, y = p, or, for a launch with a work order,
+// one workgroup per unit of a 1-D grid (below). Wave w serves KV head w % HW and,
 // of the partition's blocks, those with index = w / HW modulo 8 / HW. With
 // HW = 8 every wave streams one head through all blocks, so the 8 head
 // slices of each pool block (one contiguous block of all heads) are read by
