@@ -602,6 +602,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(AttnArgs a, cons
 // kernel would attend from its grid position.
 constexpr int kOrderBuckets = 256;
 constexpr int kOrderThreads = 1024;
+constexpr int kOrderKeep = 8;  // sequences per thread kept in registers (all of them up to 8,192)
 
 __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(AttnArgs a, int hw) {
   __shared__ int32_t count[kOrderBuckets];
@@ -612,39 +613,65 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(AttnArgs a,
   const int PT = static_cast<int>(a.part_tokens);
   const int64_t max_len = a.MB * kBlockTokens;
   for (int i = tid; i < kOrderBuckets; i += kOrderThreads) count[i] = 0;
+  // Sequence tid + k * kOrderThreads's query rows, length and cached context:
+  // the first kOrderKeep in registers, loaded together (one round trip for
+  // both passes), any further ones loaded where they are used.
+  int rq0[kOrderKeep], rq1[kOrderKeep], rlen[kOrderKeep], rctx[kOrderKeep];
+#pragma unroll
+  for (int k = 0; k < kOrderKeep; ++k) {
+    const int64_t s = tid + int64_t(k) * kOrderThreads;
+    const bool in = s < a.S;
+    rq0[k] = in ? a.qsl[s] : 0;
+    rq1[k] = in ? a.qsl[s + 1] : 0;
+    rlen[k] = in ? a.seq_lens[s] : 0;
+    rctx[k] = in ? a.ctx_lens[s] : 0;
+  }
   __syncthreads();
-  // Partitions of sequence s that the decode kernel attends (0 if none).
-  auto parts_of = [&](int64_t s, int& q0, int& q1, int& len) {
-    q0 = a.qsl[s];
-    q1 = a.qsl[s + 1];
+  // Partitions of a sequence that the decode kernel attends (0 if none), and
+  // its clamped length.
+  auto parts_of = [&](int q0, int q1, int len_raw, int& len) {
     if (!decode_path(q1 - q0, G) || q0 < 0 || q1 > a.T) return 0;
-    len = static_cast<int>(min(max(static_cast<int64_t>(a.seq_lens[s]), int64_t(0)), max_len));
+    len = static_cast<int>(min(max(static_cast<int64_t>(len_raw), int64_t(0)), max_len));
     return (len + PT - 1) / PT;
   };
   // class of a partition of `tok` tokens (1 .. PT): 0 for the longest
   auto bucket = [&](int tok) { return kOrderBuckets - 1 - (tok - 1) * kOrderBuckets / PT; };
-  for (int64_t s = tid; s < a.S; s += kOrderThreads) {
-    int q0, q1, len;
-    const int np = parts_of(s, q0, q1, len);
-    for (int p = 0; p < np; ++p) atomicAdd(&count[bucket(min(PT, len - p * PT))], n_hg);
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < kOrderBuckets; ++i) {
-      next[i] = run;
-      run += count[i];
+  // f(s, q0, q1, len_raw, ctx) for every sequence of this thread
+  auto each_seq = [&](auto f) {
+#pragma unroll
+    for (int k = 0; k < kOrderKeep; ++k) {
+      const int64_t s = tid + int64_t(k) * kOrderThreads;
+      if (s < a.S) f(s, rq0[k], rq1[k], rlen[k], rctx[k]);
     }
-    a.dorder[0] = run;
-    a.dorder[1] = 0;  // the decode's claim counter
+    for (int64_t s = tid + int64_t(kOrderKeep) * kOrderThreads; s < a.S; s += kOrderThreads)
+      f(s, a.qsl[s], a.qsl[s + 1], a.seq_lens[s], a.ctx_lens[s]);
+  };
+  each_seq([&](int64_t, int q0, int q1, int len_raw, int) {
+    int len = 0;
+    const int np = parts_of(q0, q1, len_raw, len);
+    for (int p = 0; p < np; ++p) atomicAdd(&count[bucket(min(PT, len - p * PT))], n_hg);
+  });
+  __syncthreads();
+  // Each class's first place: an exclusive scan of the counts, in place over
+  // kOrderBuckets threads (Hillis-Steele: every round reads before any
+  // thread writes).
+  const int own = tid < kOrderBuckets ? count[tid] : 0;
+  for (int off = 1; off < kOrderBuckets; off <<= 1) {
+    const int add = tid < kOrderBuckets && tid >= off ? count[tid - off] : 0;
+    __syncthreads();
+    if (tid < kOrderBuckets) count[tid] += add;
+    __syncthreads();
+  }
+  if (tid < kOrderBuckets) next[tid] = count[tid] - own;
+  if (tid == kOrderBuckets - 1) {
+    a.dorder[0] = count[tid];  // units in all
+    a.dorder[1] = 0;           // the decode's claim counter
   }
   __syncthreads();
   int4* const rec = reinterpret_cast<int4*>(a.dorder + kDecodeOrderHeader);
-  for (int64_t s = tid; s < a.S; s += kOrderThreads) {
-    int q0, q1, len;
-    const int np = parts_of(s, q0, q1, len);
-    if (np == 0) continue;
-    const int ctx = a.ctx_lens[s], len_raw = a.seq_lens[s];
+  each_seq([&](int64_t s, int q0, int q1, int len_raw, int ctx) {
+    int len = 0;
+    const int np = parts_of(q0, q1, len_raw, len);
     for (int p = 0; p < np; ++p) {
       const int at = atomicAdd(&next[bucket(min(PT, len - p * PT))], n_hg);
       for (int hg = 0; hg < n_hg; ++hg) {
@@ -652,7 +679,7 @@ __global__ __launch_bounds__(kOrderThreads) void decode_order_kernel(AttnArgs a,
         rec[2 * (at + hg) + 1] = make_int4(len_raw, ctx, 0, 0);
       }
     }
-  }
+  });
 }
 
 // Whether a decode launch takes the work order: more units than one round of
