@@ -288,6 +288,7 @@ ORDER_CASES = [  # (dtype, Hq, Hkv, D, decodes, longest context, seed): more uni
     ("bf16", 8, 2, 128, 400, 8000, 81),   # one head group per sequence, up to 2 partitions of 4096
     ("bf16", 16, 16, 64, 150, 10000, 82),  # two head groups (16 KV heads), up to 3 partitions of 4096
     ("f32", 8, 2, 64, 600, 8000, 83),
+    ("bf16", 8, 2, 64, 9000, 1000, 84),  # more sequences than the order kernel keeps in registers (8,192)
 ]
 
 
